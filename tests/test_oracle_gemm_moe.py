@@ -1,0 +1,160 @@
+"""Pins of the fp64 GEMM / MoE references and of the oracle router.
+
+GEMM: y[B,N] = deq(a)[B,K] . deq(w)[N,K]^T ("Fused Nvfp4 GEMM All Reduce
+Plugin", Baked-weight inputs and Output).  Pinned by a plain triple loop on
+tiny operands and by closed forms (identity, permutation and all-ones weights).
+
+Router: sigmoid group-top-k with a correction bias ("Nvfp4 A16 Blackwell Moe
+Runner", Nvfp4A16BlackwellMoeParams).  Pinned by exhaustive enumeration of all
+group and expert subsets on small cases, by the tie rule, and by invariants.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import synth_inputs as si
+
+
+def _quant_pair(oracle, B, N, K, seed):
+    a = si.bf16_normal((B, K), 1.0, 98, 0, seed)
+    w = si.bf16_normal((N, K), 0.02, 98, 1, seed)
+    qa = oracle.quantize(a)
+    qw = oracle.quantize(w, group_rows=N)
+    return qa, qw
+
+
+def test_gemm_matmul_equals_triple_loop(oracle):
+    qa, qw = _quant_pair(oracle, 3, 5, 48, 0)
+    A = oracle.dequant_act(qa["codes"], qa["scale"])
+    W = oracle.dequant_weight(qw["codes"], qw["sf"], qw["g_dec"][0])
+    y = oracle.gemm_ref(qa["codes"], qa["scale"], qw["codes"], qw["sf"], qw["g_dec"][0])
+    y2 = oracle.gemm_ref_loops(A, W)
+    assert np.allclose(y, y2, rtol=1e-12, atol=1e-15)
+
+
+def _unit_weight(N, K, pattern):
+    """Weights whose dequantized value is exactly `pattern` (entries 0/1):
+    code 2 (=1.0) where pattern is 1, E4M3 scale 0x38 (=1.0), global 1.0."""
+    nib = np.where(pattern > 0, 2, 0).astype(np.uint8)
+    codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    sf = np.full((N, K // 16), 0x38, np.uint8)
+    return codes, sf, np.float32(1.0)
+
+
+def test_gemm_closed_forms(oracle):
+    B, K = 4, 64
+    qa, _ = _quant_pair(oracle, B, 8, K, 1)
+    A = oracle.dequant_act(qa["codes"], qa["scale"])
+    # identity
+    wc, ws, wg = _unit_weight(K, K, np.eye(K))
+    y = oracle.gemm_ref(qa["codes"], qa["scale"], wc, ws, wg)
+    assert np.array_equal(y, A)
+    # permutation: output column n reads weight row n
+    perm = np.random.default_rng(0).permutation(K)
+    P = np.zeros((K, K)); P[np.arange(K), perm] = 1
+    wc, ws, wg = _unit_weight(K, K, P)
+    y = oracle.gemm_ref(qa["codes"], qa["scale"], wc, ws, wg)
+    assert np.array_equal(y, A[:, perm])
+    # all ones: row sums
+    wc, ws, wg = _unit_weight(3, K, np.ones((3, K)))
+    y = oracle.gemm_ref(qa["codes"], qa["scale"], wc, ws, wg)
+    assert np.allclose(y, np.repeat(A.sum(axis=1, keepdims=True), 3, axis=1), rtol=1e-14)
+    # the global weight scale multiplies every output
+    y2 = oracle.gemm_ref(qa["codes"], qa["scale"], wc, ws, np.float32(0.25))
+    assert np.array_equal(y2, y * 0.25)
+
+
+def test_dequant_weight_uses_block_scale_per_16(oracle):
+    wc, ws, wg = _unit_weight(2, 64, np.ones((2, 64)))
+    ws = ws.copy(); ws[1, 2] = 0x40                      # 2.0 on row 1, block 2
+    W = oracle.dequant_weight(wc, ws, wg)
+    assert np.all(W[0] == 1.0)
+    assert np.all(W[1, 32:48] == 2.0) and np.all(W[1, :32] == 1.0) and np.all(W[1, 48:] == 1.0)
+
+
+# ---------------------------------------------------------------- router
+
+def _brute_route(s, b, top_k, n_group, topk_group):
+    """Exhaustive: the kept groups are the group subset whose sorted score
+    vector is largest; the chosen experts the subset (inside kept groups) whose
+    sorted biased-score vector is largest; output in decreasing score order."""
+    E = len(b)
+    gsz = E // n_group
+    gscore = []
+    for g in range(n_group):
+        v = sorted(b[g * gsz:(g + 1) * gsz], reverse=True)
+        gscore.append(np.float32(v[0]) + np.float32(v[1]) if gsz > 1 else np.float32(v[0]))
+    best_groups = max(itertools.combinations(range(n_group), topk_group),
+                      key=lambda gs: sorted((gscore[g] for g in gs), reverse=True))
+    cand = [e for e in range(E) if e // gsz in best_groups]
+    best = max(itertools.combinations(cand, top_k),
+               key=lambda es: sorted((b[e] for e in es), reverse=True))
+    return sorted(best, key=lambda e: -b[e])
+
+
+@pytest.mark.parametrize("E,n_group,topk_group,top_k", [(8, 2, 1, 3), (12, 4, 2, 4), (16, 4, 3, 5)])
+def test_route_exhaustive_small(oracle, E, n_group, topk_group, top_k):
+    rng = np.random.default_rng(E)
+    T = 40
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    bias = (rng.standard_normal(E) * 0.1).astype(np.float32)
+    ids, w = oracle.route(logits, bias, top_k, n_group, topk_group, True, 1.0)
+    for t in range(T):
+        s = [oracle.sigmoid_f32(float(v)) for v in logits[t]]
+        b = [np.float32(np.float32(si_) + bias[e]) for e, si_ in enumerate(s)]
+        want = _brute_route(s, b, top_k, n_group, topk_group)
+        assert list(ids[t]) == want, t
+        ws = np.array([s[e] for e in want], np.float32)
+        assert np.allclose(w[t], ws / ws.sum(), rtol=1e-6)
+
+
+def test_route_ties_go_to_lower_index(oracle):
+    logits = np.zeros((2, 16), np.float32)
+    bias = np.zeros(16, np.float32)
+    ids, w = oracle.route(logits, bias, 3, 4, 2, True, 2.5)
+    assert ids.tolist() == [[0, 1, 2], [0, 1, 2]]
+    assert np.allclose(w, 2.5 / 3, rtol=1e-6)
+
+
+def test_route_invariants_c5_shape(oracle):
+    d = si.moe_inputs(weights=False)
+    c = si.CONFIGS["C5"]
+    ids, w = oracle.route(d["logits"], d["bias"], c["top_k"], c["n_group"], c["topk_group"],
+                          c["norm_topk_prob"], c["routed_scaling"])
+    gsz = c["E"] // c["n_group"]
+    for t in range(c["T"]):
+        assert len(set(ids[t].tolist())) == c["top_k"]
+        assert len({int(e) // gsz for e in ids[t]}) <= c["topk_group"]
+        assert abs(float(w[t].sum()) - c["routed_scaling"]) < 1e-5
+        b = [np.float32(oracle.sigmoid_f32(float(v))) + d["bias"][e] for e, v in enumerate(d["logits"][t])]
+        assert all(b[ids[t][j]] >= b[ids[t][j + 1]] for j in range(c["top_k"] - 1))
+
+
+def test_route_without_normalisation_returns_sigmoid(oracle):
+    rng = np.random.default_rng(3)
+    logits = rng.standard_normal((5, 16)).astype(np.float32)
+    bias = np.zeros(16, np.float32)
+    ids, w = oracle.route(logits, bias, 4, 4, 2, False, 1.5)
+    for t in range(5):
+        for j in range(4):
+            assert w[t, j] == np.float32(np.float32(oracle.sigmoid_f32(float(logits[t, ids[t, j]]))) * np.float32(1.5))
+
+
+def test_moe_ref_closed_form(oracle):
+    # fc1 and fc2 equal to identity: out_t = sum_j w_tj * relu(x_t)^2
+    H = 32
+    T, E, top_k = 6, 4, 2
+    x = torch.from_numpy(np.random.default_rng(4).standard_normal((T, H)).astype(np.float32)).half()
+    wc, ws, _ = _unit_weight(H, H, np.eye(H))
+    w1c = np.stack([wc] * E); w1s = np.stack([ws] * E); g = np.ones(E, np.float32)
+    ids = np.array([[t % E, (t + 1) % E] for t in range(T)], np.int32)
+    wts = np.full((T, top_k), 0.5, np.float32)
+    out = oracle.moe_ref(x.numpy(), ids, wts, w1c, w1s, g, w1c, w1s, g)
+    xr = np.maximum(x.double().numpy(), 0) ** 2
+    assert np.allclose(out, xr, rtol=1e-14)
+    # expert global scales multiply fc1 (squared by ReLU^2) and fc2 outputs
+    g1 = np.full(E, 2.0, np.float32); g2 = np.full(E, 3.0, np.float32)
+    out2 = oracle.moe_ref(x.numpy(), ids, wts, w1c, w1s, g1, w1c, w1s, g2)
+    assert np.allclose(out2, xr * 4.0 * 3.0, rtol=1e-14)
