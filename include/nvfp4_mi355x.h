@@ -1,0 +1,168 @@
+/*
+ * nvfp4_mi355x.h -- C ABI of the MI355X (gfx950) NVFP4 hot path.
+ *
+ * NVFP4 in this library: values in 16-element K-blocks; each block stores 16
+ * E2M1 (FP4) codes packed two per byte (element 2i in bits 3..0, element 2i+1
+ * in bits 7..4), one FP8-E4M3 block scale byte, and shares one FP32 global
+ * scale per row (per token), per tensor or per expert.  The format and operand
+ * shapes follow "Fused Nvfp4 GEMM All Reduce Plugin" (TensorRT-Edge-LLM C++
+ * API), section "Baked-weight inputs": activation FP4 [B,K], activation_scale
+ * FP32 [B,1,K/16] (the combined scale from DequantizeLinear), weight FP4 [N,K],
+ * weight FP8 block scale [N,K/16], scalar FP32 global weight scale, FP16 [B,N]
+ * output.  Per-token activation globals follow "perf: optimize per-token nvfp4
+ * quantization kernel" (flashinfer pull request 3237), description.
+ *
+ * Quantization arithmetic (binary32, round-to-nearest-even, exact division):
+ *   amax    = max |y| over the global group
+ *   g_enc   = 2688 / amax   (2688 = 448 * 6), replaced by FLT_MAX if not finite
+ *   g_dec   = 1 / g_enc     -- the FP32 global scale that is stored
+ *   per block: sf = E4M3_RNE(min((amax_b / 6) * g_enc, 448))
+ *              c  = e4m3(sf) * g_dec        -- combined scale, [rows,1,K/16]
+ *              enc = (c == 0) ? 0 : 1 / c
+ *   per element: code = E2M1_RNE_saturating(y * enc), sign kept (-0 -> 0x8)
+ * Dequantization: activation x = e2m1(code) * c; weight w = e2m1(code) *
+ * e4m3(sf) * g_dec.
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless stated; the caller allocates every
+ *    buffer and keeps it alive until the stream work completes.  The library
+ *    never allocates, frees or keeps a pointer past the call.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls are asynchronous and stream-ordered; they never synchronize.
+ *  - Arguments are validated on the host before anything is launched: on any
+ *    error status nothing has been written.  Kernel faults surface at the
+ *    caller's next synchronization.
+ *  - Rows and strides are dense and row-major; leading dimensions are
+ *    flattened into rows by the caller.  Offsets are 64-bit.
+ *  - Inputs that are not 16-byte aligned take a scalar path with identical
+ *    results ("Building Custom TensorRT-LLM Plugins for Low-Latency FP8
+ *    Inference at Scale", "Production Pitfalls & Hard Lessons", item 1).
+ *  - Re-entrant; no mutable state besides a per-device property cache filled
+ *    on first use.  Temporary memory comes from the caller's workspace
+ *    (same article, item 3).
+ */
+#ifndef NVFP4_MI355X_H
+#define NVFP4_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define NVFP4_OK 0
+#define NVFP4_EINVAL 1        /* null pointer, bad size, bad enum, K % 16 != 0 */
+#define NVFP4_EUNSUPPORTED 2  /* current device is not gfx950, or size beyond limits */
+#define NVFP4_EWORKSPACE 3    /* workspace missing or smaller than the query returns */
+#define NVFP4_EHIP 4          /* a HIP runtime call or launch failed */
+
+/* Input element types. */
+#define NVFP4_BF16 0
+#define NVFP4_FP16 1
+
+/* Activations fused in front of the quantizer. */
+#define NVFP4_ACT_NONE 0
+#define NVFP4_ACT_SWIGLU 1    /* y = silu(gate) * up; gate = first half of the row */
+#define NVFP4_ACT_RELU2 2     /* y = max(x, 0)^2 */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* nvfp4_status_string(int32_t status);
+
+/*
+ * nvfp4_quantize -- NVFP4-quantize x[rows, k] with one FP32 global per group
+ * of `group_rows` consecutive rows: 1 = per token (activations), rows = per
+ * tensor (the scalar weight_f32_scale of the plugin contract), rows/E = per
+ * expert ("Nvfp4 A16 Blackwell Moe Runner", globalScales [E]).
+ *   x          : [rows, k] bf16 or fp16 (dtype), device
+ *   codes      : [rows, k/2] uint8 out
+ *   sf         : [rows, k/16] uint8 out (E4M3 bytes)
+ *   g_dec      : [rows / group_rows] float out (stored global scale)
+ *   scale_out  : [rows, k/16] float out, combined scale c; may be NULL
+ *   workspace  : device scratch of nvfp4_quantize_workspace_size() bytes
+ *                (0 bytes when group_rows == 1; then may be NULL)
+ * Requires rows >= 0, k > 0, k % 16 == 0, group_rows >= 1 dividing rows.
+ * rows == 0 is a no-op.
+ */
+int32_t nvfp4_quantize(const void* x, int32_t dtype, int64_t rows, int64_t k, int64_t group_rows,
+                       uint8_t* codes, uint8_t* sf, float* g_dec, float* scale_out,
+                       void* workspace, size_t workspace_bytes, void* stream);
+size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t k, int64_t group_rows);
+
+/*
+ * nvfp4_act_quant -- fused activation + per-token NVFP4 quantization: the
+ * activation is evaluated in fp32 registers and never written back
+ * ("Building Custom TensorRT-LLM Plugins for Low-Latency FP8 Inference at
+ * Scale", "The Cost of Non-Fused Quantization" and "Fusing the Kernel in CUDA";
+ * ReLU2 from "Nvfp4 A16 Blackwell Moe Runner").
+ *   x       : [rows, 2*k_out] for SWIGLU (gate | up), else [rows, k_out]
+ *   codes   : [rows, k_out/2], sf: [rows, k_out/16], g_dec: [rows],
+ *   scale_out: [rows, k_out/16] or NULL.
+ * SwiGLU's exp is a fixed binary32 evaluation: for x > 88.75 it is +inf, for
+ * x < -87 it is 0, else with n = rint(x * fp32(log2 e)),
+ * r = fma(-n, fp32(ln 2), x), r = fma(-n, fp32(ln 2 - fp32(ln 2)), r),
+ * p = Horner-with-fma of sum_{k<=7} fp32(1/k!) r^k, result ldexp(p, n);
+ * then silu(g) = g / (1 + exp(-g)) with exact division.
+ * Requires k_out % 16 == 0, rows >= 0.
+ */
+int32_t nvfp4_act_quant(const void* x, int32_t dtype, int64_t rows, int64_t k_out, int32_t act,
+                        uint8_t* codes, uint8_t* sf, float* g_dec, float* scale_out, void* stream);
+
+/*
+ * nvfp4_gemm -- y[B,N] (fp16) = sum_k deq(a)[B,k] * deq(w)[N,k], the GEMM of
+ * "Fused Nvfp4 GEMM All Reduce Plugin" (baked-weight inputs 0..4, output 0)
+ * on one rank's K-share; the all-reduce is not part of this library.
+ *   a        : [B, K/2] uint8 activation codes
+ *   a_scale  : [B, K/16] float combined activation scale ([B,1,K/16])
+ *   w        : [N, K/2] uint8 weight codes
+ *   w_sf     : [N, K/16] uint8 E4M3 weight block scales
+ *   w_gscale : pointer to ONE float on the device, the global weight scale
+ *   y        : [B, N] fp16 out (round-to-nearest-even from fp32 accumulation)
+ *   workspace: nvfp4_gemm_workspace_size() bytes (may be 0 -> NULL allowed)
+ * Requires B >= 0, N > 0, K > 0, K % 32 == 0 (whole bytes of 16-blocks in
+ * pairs).  B == 0 is a no-op.
+ */
+int32_t nvfp4_gemm(const uint8_t* a, const float* a_scale, const uint8_t* w, const uint8_t* w_sf,
+                   const float* w_gscale, void* y, int64_t B, int64_t N, int64_t K,
+                   void* workspace, size_t workspace_bytes, void* stream);
+size_t nvfp4_gemm_workspace_size(int64_t B, int64_t N, int64_t K);
+
+/*
+ * nvfp4_moe_w4a16 -- routed MoE layer with NVFP4 weights and FP16
+ * activations ("Nvfp4 A16 Blackwell Moe Runner", Nvfp4A16BlackwellMoeParams):
+ * sigmoid group-top-k routing with a correction bias, then per chosen expert
+ * out_t += w_tj * (relu(x_t . W1_e^T)^2) . W2_e^T.
+ *   router_logits   : [tokens, experts] float
+ *   correction_bias : [experts] float (used for selection only)
+ *   x               : [tokens, hidden] fp16
+ *   w1, w1_sf, w1_g : [experts, inter, hidden/2] u8, [experts, inter, hidden/16] u8,
+ *                     [experts] float  (fc1, per-expert global)
+ *   w2, w2_sf, w2_g : [experts, hidden, inter/2] u8, [experts, hidden, inter/16] u8,
+ *                     [experts] float  (fc2)
+ *   out             : [tokens, hidden] fp16
+ *   topk_ids_out    : [tokens, top_k] int32 or NULL (chosen experts, best first)
+ *   topk_w_out      : [tokens, top_k] float or NULL (their weights)
+ * Routing: s = 1/(1+exp(-l)) (exp as for nvfp4_act_quant), b = s + bias;
+ * group score = sum of the group's two best b; keep topk_group groups; pick
+ * top_k experts by b inside them (ties to the lower index); weights s, divided
+ * by their sum when norm_topk_prob, times routed_scaling.
+ * Requires experts % n_group == 0, 1 <= topk_group <= n_group,
+ * 1 <= top_k <= topk_group * experts / n_group, top_k <= 16, experts <= 256,
+ * hidden % 32 == 0, inter % 32 == 0.
+ */
+int32_t nvfp4_moe_w4a16(const float* router_logits, const float* correction_bias, const void* x,
+                        const uint8_t* w1, const uint8_t* w1_sf, const float* w1_g,
+                        const uint8_t* w2, const uint8_t* w2_sf, const float* w2_g, void* out,
+                        int32_t* topk_ids_out, float* topk_w_out,
+                        int32_t tokens, int32_t experts, int32_t top_k, int32_t hidden, int32_t inter,
+                        int32_t n_group, int32_t topk_group, int32_t norm_topk_prob,
+                        float routed_scaling, void* workspace, size_t workspace_bytes, void* stream);
+size_t nvfp4_moe_w4a16_workspace_size(int32_t tokens, int32_t experts, int32_t top_k, int32_t hidden,
+                                      int32_t inter);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_MI355X_H */

@@ -1,0 +1,189 @@
+"""Python binding of libnvfp4_mi355x.so (the C ABI in include/nvfp4_mi355x.h).
+
+Argument marshalling only: every step of the NVFP4 path runs in the HIP
+kernels of the shared library.  torch supplies device memory and the current
+HIP stream.  There is no CPU fallback: if the library is missing the import
+fails, and every call checks the library's status code.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4_mi355x.so")
+
+NVFP4_OK, NVFP4_EINVAL, NVFP4_EUNSUPPORTED, NVFP4_EWORKSPACE, NVFP4_EHIP = range(5)
+NVFP4_BF16, NVFP4_FP16 = 0, 1
+ACT = {"none": 0, "swiglu": 1, "relu2": 2}
+
+EXPORTS = [
+    "nvfp4_status_string", "nvfp4_quantize", "nvfp4_quantize_workspace_size", "nvfp4_act_quant",
+    "nvfp4_gemm", "nvfp4_gemm_workspace_size", "nvfp4_moe_w4a16", "nvfp4_moe_w4a16_workspace_size",
+]
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (what, _lib.nvfp4_status_string(status).decode(), status))
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libnvfp4_mi355x.so is not built; run nvfp4_block_scaled_quantize_amd/build.py "
+                          "(hipcc, gfx950) first -- there is no fallback implementation")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i32, i64, sz, f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                            ctypes.c_float)
+    L.nvfp4_status_string.argtypes = [i32]; L.nvfp4_status_string.restype = ctypes.c_char_p
+    L.nvfp4_quantize.argtypes = [p, i32, i64, i64, i64, p, p, p, p, p, sz, p]
+    L.nvfp4_quantize.restype = i32
+    L.nvfp4_quantize_workspace_size.argtypes = [i64, i64, i64]
+    L.nvfp4_quantize_workspace_size.restype = sz
+    L.nvfp4_act_quant.argtypes = [p, i32, i64, i64, i32, p, p, p, p, p]
+    L.nvfp4_act_quant.restype = i32
+    L.nvfp4_gemm.argtypes = [p, p, p, p, p, p, i64, i64, i64, p, sz, p]
+    L.nvfp4_gemm.restype = i32
+    L.nvfp4_gemm_workspace_size.argtypes = [i64, i64, i64]
+    L.nvfp4_gemm_workspace_size.restype = sz
+    L.nvfp4_moe_w4a16.argtypes = [p, p, p, p, p, p, p, p, p, p, p, p,
+                                  i32, i32, i32, i32, i32, i32, i32, i32, f32, p, sz, p]
+    L.nvfp4_moe_w4a16.restype = i32
+    L.nvfp4_moe_w4a16_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    L.nvfp4_moe_w4a16_workspace_size.restype = sz
+    return L
+
+
+_lib = _load()
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on the GPU")
+
+
+def _dtype_code(x: torch.Tensor) -> int:
+    if x.dtype == torch.bfloat16:
+        return NVFP4_BF16
+    if x.dtype == torch.float16:
+        return NVFP4_FP16
+    raise TypeError("input must be bfloat16 or float16")
+
+
+def _workspace(nbytes: int, device, workspace: torch.Tensor | None):
+    if nbytes == 0:
+        return None, 0
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small: need %d bytes" % nbytes)
+        return workspace, workspace.numel() * workspace.element_size()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def quantize(x: torch.Tensor, group_rows: int = 1, want_scale: bool = True, out: dict | None = None,
+             workspace: torch.Tensor | None = None, stream=None) -> dict:
+    """NVFP4-quantize x [rows, k] with one global scale per `group_rows` rows."""
+    _check_dev(x)
+    rows, k = x.shape
+    dev = x.device
+    o = out or {
+        "codes": torch.empty((rows, k // 2), dtype=torch.uint8, device=dev),
+        "sf": torch.empty((rows, k // 16), dtype=torch.uint8, device=dev),
+        "g_dec": torch.empty((rows // max(group_rows, 1),), dtype=torch.float32, device=dev),
+        "scale": torch.empty((rows, k // 16), dtype=torch.float32, device=dev) if want_scale else None,
+    }
+    ws, wsb = _workspace(_lib.nvfp4_quantize_workspace_size(rows, k, group_rows), dev, workspace)
+    st = _lib.nvfp4_quantize(_ptr(x), _dtype_code(x), rows, k, group_rows, _ptr(o["codes"]), _ptr(o["sf"]),
+                             _ptr(o["g_dec"]), _ptr(o.get("scale")), _ptr(ws), wsb, _stream(stream))
+    if st != NVFP4_OK:
+        raise Nvfp4Error(st, "nvfp4_quantize")
+    return o
+
+
+def act_quant(x: torch.Tensor, act: str = "none", want_scale: bool = True, out: dict | None = None,
+              stream=None) -> dict:
+    """Fused activation (none / swiglu / relu2) + per-token NVFP4 quantization."""
+    _check_dev(x)
+    rows, k_in = x.shape
+    a = ACT[act] if isinstance(act, str) else int(act)
+    k_out = k_in // 2 if a == ACT["swiglu"] else k_in
+    dev = x.device
+    o = out or {
+        "codes": torch.empty((rows, k_out // 2), dtype=torch.uint8, device=dev),
+        "sf": torch.empty((rows, k_out // 16), dtype=torch.uint8, device=dev),
+        "g_dec": torch.empty((rows,), dtype=torch.float32, device=dev),
+        "scale": torch.empty((rows, k_out // 16), dtype=torch.float32, device=dev) if want_scale else None,
+    }
+    st = _lib.nvfp4_act_quant(_ptr(x), _dtype_code(x), rows, k_out, a, _ptr(o["codes"]), _ptr(o["sf"]),
+                              _ptr(o["g_dec"]), _ptr(o.get("scale")), _stream(stream))
+    if st != NVFP4_OK:
+        raise Nvfp4Error(st, "nvfp4_act_quant")
+    return o
+
+
+def gemm_workspace_size(B: int, N: int, K: int) -> int:
+    return int(_lib.nvfp4_gemm_workspace_size(B, N, K))
+
+
+def gemm(a_codes: torch.Tensor, a_scale: torch.Tensor, w_codes: torch.Tensor, w_sf: torch.Tensor,
+         w_g: torch.Tensor, out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+         stream=None) -> torch.Tensor:
+    """y[B, N] fp16 = deq(a) . deq(w)^T."""
+    _check_dev(a_codes, a_scale, w_codes, w_sf, w_g)
+    B, K = a_codes.shape[0], a_codes.shape[1] * 2
+    N = w_codes.shape[0]
+    if w_codes.shape[1] * 2 != K or a_scale.shape != (B, K // 16) or w_sf.shape != (N, K // 16):
+        raise ValueError("operand shapes do not match the plugin contract")
+    if a_scale.dtype != torch.float32 or w_g.dtype != torch.float32 or w_g.numel() < 1:
+        raise TypeError("a_scale and w_g must be float32 (w_g holds one value)")
+    y = out if out is not None else torch.empty((B, N), dtype=torch.float16, device=a_codes.device)
+    ws, wsb = _workspace(gemm_workspace_size(B, N, K), a_codes.device, workspace)
+    st = _lib.nvfp4_gemm(_ptr(a_codes), _ptr(a_scale), _ptr(w_codes), _ptr(w_sf), _ptr(w_g), _ptr(y),
+                         B, N, K, _ptr(ws), wsb, _stream(stream))
+    if st != NVFP4_OK:
+        raise Nvfp4Error(st, "nvfp4_gemm")
+    return y
+
+
+def moe_workspace_size(tokens, experts, top_k, hidden, inter) -> int:
+    return int(_lib.nvfp4_moe_w4a16_workspace_size(tokens, experts, top_k, hidden, inter))
+
+
+def moe_w4a16(logits, bias, x, w1, w1_sf, w1_g, w2, w2_sf, w2_g, top_k, n_group, topk_group,
+              norm_topk_prob=True, routed_scaling=1.0, out=None, want_routing=False,
+              workspace=None, stream=None):
+    """Routed W4A16 MoE layer; returns out (and (ids, weights) if want_routing)."""
+    _check_dev(logits, bias, x, w1, w1_sf, w1_g, w2, w2_sf, w2_g)
+    T, E = logits.shape
+    hidden = x.shape[1]
+    inter = w1.shape[1]
+    if x.dtype != torch.float16:
+        raise TypeError("hidden states must be float16")
+    o = out if out is not None else torch.empty((T, hidden), dtype=torch.float16, device=x.device)
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=x.device) if want_routing else None
+    wts = torch.empty((T, top_k), dtype=torch.float32, device=x.device) if want_routing else None
+    ws, wsb = _workspace(moe_workspace_size(T, E, top_k, hidden, inter), x.device, workspace)
+    st = _lib.nvfp4_moe_w4a16(_ptr(logits), _ptr(bias), _ptr(x), _ptr(w1), _ptr(w1_sf), _ptr(w1_g),
+                              _ptr(w2), _ptr(w2_sf), _ptr(w2_g), _ptr(o), _ptr(ids), _ptr(wts),
+                              T, E, top_k, hidden, inter, n_group, topk_group, int(bool(norm_topk_prob)),
+                              float(routed_scaling), _ptr(ws), wsb, _stream(stream))
+    if st != NVFP4_OK:
+        raise Nvfp4Error(st, "nvfp4_moe_w4a16")
+    return (o, ids, wts) if want_routing else o

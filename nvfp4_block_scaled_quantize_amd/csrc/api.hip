@@ -1,0 +1,161 @@
+// api.hip -- the C ABI of include/nvfp4_mi355x.h: host-side validation, the
+// per-device gfx950 check, workspace checks, and stream-ordered launches.
+// Nothing here allocates device memory, synchronizes, or keeps pointers.
+#include <mutex>
+#include <string.h>
+
+#include "../../include/nvfp4_mi355x.h"
+#include "internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// 1 if the current device is gfx950, 0 if not, -1 if HIP reports an error.
+// Device properties are queried once per device.
+int current_device_ok() {
+  static std::once_flag once[kMaxDevices];
+  static int ok[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+  std::call_once(once[dev], [dev]() {
+    hipDeviceProp_t p;
+    ok[dev] = (hipGetDeviceProperties(&p, dev) == hipSuccess &&
+               strncmp(p.gcnArchName, "gfx950", 6) == 0) ? 1 : 0;
+  });
+  return ok[dev];
+}
+
+int32_t device_status() {
+  const int d = current_device_ok();
+  if (d < 0) return NVFP4_EHIP;
+  return d ? NVFP4_OK : NVFP4_EUNSUPPORTED;
+}
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP; }
+
+bool aligned4(const void* p) { return ((uintptr_t)p % 4) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_status_string(int32_t status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_EINVAL: return "invalid argument";
+    case NVFP4_EUNSUPPORTED: return "unsupported device or size";
+    case NVFP4_EWORKSPACE: return "workspace missing or too small";
+    case NVFP4_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t k, int64_t group_rows) {
+  if (rows <= 0 || k <= 0 || group_rows <= 1 || rows % group_rows != 0) return 0;
+  const int np = nvfp4::quant_num_parts(group_rows * k);
+  return (size_t)(rows / group_rows) * (size_t)np * sizeof(float);
+}
+
+static int32_t quantize_common(const void* x, int32_t dtype, int64_t rows, int64_t k_out,
+                               int32_t act, int64_t group_rows, uint8_t* codes, uint8_t* sf,
+                               float* g_dec, float* scale_out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (dtype != NVFP4_BF16 && dtype != NVFP4_FP16) return NVFP4_EINVAL;
+  if (act != NVFP4_ACT_NONE && act != NVFP4_ACT_SWIGLU && act != NVFP4_ACT_RELU2) return NVFP4_EINVAL;
+  if (rows < 0 || k_out <= 0 || (k_out % 16) != 0 || group_rows < 1) return NVFP4_EINVAL;
+  if (rows > 0 && (rows % group_rows) != 0) return NVFP4_EINVAL;
+  if (rows == 0) return NVFP4_OK;
+  if (!x || !codes || !sf || !g_dec) return NVFP4_EINVAL;
+  if (!aligned4(g_dec) || (scale_out && !aligned4(scale_out))) return NVFP4_EINVAL;
+  if (((uintptr_t)x % 2) != 0) return NVFP4_EINVAL;
+  if (rows > 0x7FFFFFFFLL) return NVFP4_EUNSUPPORTED;                // grid.x limit
+  const int64_t k_in = (act == NVFP4_ACT_SWIGLU) ? 2 * k_out : k_out;
+  if (k_in > (int64_t)1 << 40) return NVFP4_EUNSUPPORTED;
+  nvfp4::QuantArgs a{};
+  a.x = x; a.dtype = dtype; a.act = act; a.rows = rows; a.k_out = k_out; a.group_rows = group_rows;
+  a.codes = codes; a.sf = sf; a.g_dec = g_dec; a.scale_out = scale_out; a.parts = nullptr;
+  a.nparts = 0;
+  if (group_rows > 1) {
+    if ((rows / group_rows) > 65535) return NVFP4_EUNSUPPORTED;   // grid.y limit of the partial pass
+    const size_t need = nvfp4_quantize_workspace_size(rows, k_out, group_rows);
+    if (!workspace || workspace_bytes < need || !aligned4(workspace)) return NVFP4_EWORKSPACE;
+    a.parts = (float*)workspace;
+    a.nparts = nvfp4::quant_num_parts(group_rows * k_out);
+  }
+  const int32_t ds = device_status();
+  if (ds != NVFP4_OK) return ds;
+  return hip_status(nvfp4::launch_quantize(a, (hipStream_t)stream));
+}
+
+int32_t nvfp4_quantize(const void* x, int32_t dtype, int64_t rows, int64_t k, int64_t group_rows,
+                       uint8_t* codes, uint8_t* sf, float* g_dec, float* scale_out,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return quantize_common(x, dtype, rows, k, NVFP4_ACT_NONE, group_rows, codes, sf, g_dec,
+                         scale_out, workspace, workspace_bytes, stream);
+}
+
+int32_t nvfp4_act_quant(const void* x, int32_t dtype, int64_t rows, int64_t k_out, int32_t act,
+                        uint8_t* codes, uint8_t* sf, float* g_dec, float* scale_out, void* stream) {
+  return quantize_common(x, dtype, rows, k_out, act, 1, codes, sf, g_dec, scale_out, nullptr, 0,
+                         stream);
+}
+
+size_t nvfp4_gemm_workspace_size(int64_t B, int64_t N, int64_t K) {
+  if (B <= 0 || N <= 0 || K <= 0) return 0;
+  return nvfp4::gemm_workspace_bytes(B, N, K);
+}
+
+int32_t nvfp4_gemm(const uint8_t* a, const float* a_scale, const uint8_t* w, const uint8_t* w_sf,
+                   const float* w_gscale, void* y, int64_t B, int64_t N, int64_t K,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || N <= 0 || K <= 0 || (K % 32) != 0) return NVFP4_EINVAL;
+  if (B == 0) return NVFP4_OK;
+  if (!a || !a_scale || !w || !w_sf || !w_gscale || !y) return NVFP4_EINVAL;
+  if (!aligned4(a_scale) || !aligned4(w_gscale) || ((uintptr_t)y % 2) != 0) return NVFP4_EINVAL;
+  if (((uintptr_t)w % 16) != 0 || ((uintptr_t)w_sf % 2) != 0) return NVFP4_EINVAL;
+  if (B > 0x7FFFFFFFLL || N > 0x7FFFFFFFLL || K > 0x7FFFFFFFLL) return NVFP4_EUNSUPPORTED;
+  const size_t need = nvfp4::gemm_workspace_bytes(B, N, K);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return NVFP4_EWORKSPACE;
+  const int32_t ds = device_status();
+  if (ds != NVFP4_OK) return ds;
+  nvfp4::GemmArgs g{a, a_scale, w, w_sf, w_gscale, y, B, N, K, workspace, workspace_bytes};
+  return hip_status(nvfp4::launch_gemm(g, (hipStream_t)stream));
+}
+
+size_t nvfp4_moe_w4a16_workspace_size(int32_t tokens, int32_t experts, int32_t top_k,
+                                      int32_t hidden, int32_t inter) {
+  if (tokens <= 0 || experts <= 0 || top_k <= 0 || hidden <= 0 || inter <= 0) return 0;
+  return nvfp4::moe_workspace_bytes(tokens, experts, top_k, hidden, inter);
+}
+
+int32_t nvfp4_moe_w4a16(const float* router_logits, const float* correction_bias, const void* x,
+                        const uint8_t* w1, const uint8_t* w1_sf, const float* w1_g,
+                        const uint8_t* w2, const uint8_t* w2_sf, const float* w2_g, void* out,
+                        int32_t* topk_ids_out, float* topk_w_out, int32_t tokens, int32_t experts,
+                        int32_t top_k, int32_t hidden, int32_t inter, int32_t n_group,
+                        int32_t topk_group, int32_t norm_topk_prob, float routed_scaling,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (tokens < 0 || experts <= 0 || experts > 256 || n_group <= 0 || experts % n_group != 0)
+    return NVFP4_EINVAL;
+  const int gsize = experts / n_group;
+  if (topk_group < 1 || topk_group > n_group || top_k < 1 || top_k > 16 ||
+      top_k > topk_group * gsize)
+    return NVFP4_EINVAL;
+  if (hidden <= 0 || inter <= 0 || hidden % 32 != 0 || inter % 32 != 0) return NVFP4_EINVAL;
+  if (tokens == 0) return NVFP4_OK;
+  if (!router_logits || !correction_bias || !x || !w1 || !w1_sf || !w1_g || !w2 || !w2_sf ||
+      !w2_g || !out)
+    return NVFP4_EINVAL;
+  const size_t need = nvfp4::moe_workspace_bytes(tokens, experts, top_k, hidden, inter);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % 256) != 0)
+    return NVFP4_EWORKSPACE;
+  const int32_t ds = device_status();
+  if (ds != NVFP4_OK) return ds;
+  nvfp4::MoeArgs m{router_logits, correction_bias, x, w1, w1_sf, w1_g, w2, w2_sf, w2_g, out,
+                   topk_ids_out, topk_w_out, tokens, experts, top_k, hidden, inter, n_group,
+                   topk_group, norm_topk_prob ? 1 : 0, routed_scaling, workspace, workspace_bytes};
+  return hip_status(nvfp4::launch_moe(m, (hipStream_t)stream));
+}
+
+}  // extern "C"

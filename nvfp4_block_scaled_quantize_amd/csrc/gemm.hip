@@ -1,0 +1,423 @@
+// gemm.hip -- block-scaled NVFP4 GEMM y[B,N] = deq(a)[B,K] . deq(w)[N,K]^T with
+// FP16 output, the operation of "Fused Nvfp4 GEMM All Reduce Plugin"
+// (baked-weight inputs 0..4, output 0), for gfx950.
+//
+// Why FP16 MFMA: gfx950's scaled f8f6f4 MFMA applies power-of-two (E8M0)
+// scales per 32 K-elements, while NVFP4 carries an E4M3 scale per 16 elements
+// and the activation side an arbitrary FP32 scale per 16 elements.  The
+// dequantized weight e2m1 * e4m3 has at most 6 significant bits and lies in
+// [2^-10, 2688], so it is EXACT in FP16; the global weight scale moves to the
+// epilogue.  The activation q * c is rounded once to FP16 after a per-row
+// power-of-two normalization (so no row can overflow FP16), and the row's
+// power of two returns in the epilogue.  Products accumulate in FP32.
+//
+// Two kernels, chosen by the batch size:
+//  * gemm_skinny (B <= 16, decode): a streaming GEMV-like pass over the weight
+//    matrix.  Each wave owns 16 weight rows and one quarter of K; every lane
+//    issues 16-byte loads of 32 consecutive FP4 codes of its row (eight loads in
+//    flight per lane), converts them with v_cvt_scalef32_pk_f16_fp4 and one
+//    packed FP16 multiply by the E4M3 scale, and feeds v_mfma_f32_16x16x32_f16
+//    with the (up to 16) activation rows as the other operand.  The activations
+//    are dequantized once per workgroup into LDS.  The four K quarters are
+//    summed in LDS in a fixed order (deterministic).
+//  * gemm_tiled (larger B, prefill): a prologue kernel writes the normalized
+//    FP16 activations once; the main kernel computes 256x256 output tiles with
+//    4 waves (128x128 each, v_mfma_f32_32x32x16_f16), staging FP16 activations
+//    and packed FP4 weight codes + E4M3 bytes through double-buffered LDS;
+//    weights are dequantized in registers right before each MFMA.
+//
+// K permutation: inside each MFMA group the hardware sums over all k of the
+// instruction, so the assignment of actual k values to MFMA k-slots is free as
+// long as both operands use the same one.  Each lane group takes 32
+// consecutive k (one 16-byte load of codes, two E4M3 bytes) and spreads them
+// over four MFMAs.
+#include "device_common.h"
+#include "internal.h"
+
+#include <mutex>
+
+namespace nvfp4 {
+
+namespace {
+
+// ------------------------------------------------------------ shared helpers
+
+// Exponent e with max_c * 2^-e in [1, 2) (0 for a zero row).
+__device__ __forceinline__ int row_exponent(float cmax) {
+  if (!(cmax > 0.0f)) return 0;
+  return (int)((__float_as_uint(cmax) >> 23) & 0xFFu) - 127;
+}
+
+// Eight FP4 codes (one dword) -> eight FP16 values q * scale16 (exact when
+// scale16 is an E4M3 value).
+__device__ __forceinline__ v8h dequant8_f16(uint32_t codes, _Float16 scale16) {
+  const v2h s2 = {scale16, scale16};
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s2;
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * s2;
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * s2;
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * s2;
+  v8h r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// Eight FP4 activation codes times an fp32 scale, each product rounded to FP16.
+__device__ __forceinline__ v8h dequant8_act(uint32_t codes, float c) {
+  const v2f q0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+  const v2f q1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+  const v2f q2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+  const v2f q3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+  v8h r;
+  r[0] = (_Float16)(q0.x * c); r[1] = (_Float16)(q0.y * c);
+  r[2] = (_Float16)(q1.x * c); r[3] = (_Float16)(q1.y * c);
+  r[4] = (_Float16)(q2.x * c); r[5] = (_Float16)(q2.y * c);
+  r[6] = (_Float16)(q3.x * c); r[7] = (_Float16)(q3.y * c);
+  return r;
+}
+
+// E4M3 byte 0 / byte 1 of a word -> FP16 (every E4M3 value is exact in FP16).
+__device__ __forceinline__ _Float16 e4m3_b0_f16(uint32_t word) {
+  return (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)word, 0);
+}
+__device__ __forceinline__ _Float16 e4m3_b1_f16(uint32_t word) {
+  return (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)word, 1);
+}
+
+__device__ __forceinline__ uint32_t load_u32_bytes(const uint8_t* p) {
+  return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+}
+
+// ------------------------------------------------------------ skinny (decode)
+
+constexpr int kSkThreads = 512;   // 8 waves
+constexpr int kSkNsub = 2;        // 16-row subtiles per workgroup
+constexpr int kSkKs = 4;          // K quarters per workgroup
+constexpr int kSkRows = 16 * kSkNsub;
+constexpr int kSkPF = 8;          // 128-k chunks loaded per round per wave
+constexpr size_t kSkRedBytes = (size_t)kSkKs * kSkRows * 16 * sizeof(float);
+constexpr size_t kMaxLds = 160 * 1024;
+
+size_t skinny_lds_bytes(int64_t B, int64_t K) {
+  return (((size_t)B * (size_t)(K + 8) * 2 + 15) / 16) * 16 + kSkRedBytes;
+}
+
+__global__ void __launch_bounds__(kSkThreads)
+gemm_skinny(const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
+            const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_sf,
+            const float* __restrict__ w_g, _Float16* __restrict__ y, int B, int N, int K) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ float rs[16];
+  __shared__ float rinv[16];
+  const int pitch = K + 8;   // halves; keeps consecutive activation rows 16 B apart in bank space
+  _Float16* As = reinterpret_cast<_Float16*>(smem);
+  float* red = reinterpret_cast<float*>(smem + (((size_t)B * pitch * 2 + 15) / 16) * 16);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nsub = wave % kSkNsub, ks = wave / kSkNsub;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int nrow = blockIdx.x * kSkRows + nsub * 16 + r16;
+  const int64_t kb2 = K / 2, kb16 = K / 16;
+  const int nchunks = (K + 127) >> 7;
+
+  // 1. weight loads of the first round (issued before the activation work)
+  const bool nvalid = nrow < N;
+  const uint8_t* wr = w + (int64_t)(nvalid ? nrow : 0) * kb2;
+  const uint8_t* sr = w_sf + (int64_t)(nvalid ? nrow : 0) * kb16;
+  uint4 wc[kSkPF];
+  uint32_t wsv[kSkPF];
+  auto load_round = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < kSkPF; ++i) {
+      const int c = c0 + i * kSkKs;
+      const int k = c * 128 + 32 * g;
+      const bool v = nvalid && c < nchunks && k < K;
+      wc[i] = v ? *reinterpret_cast<const uint4*>(wr + k / 2) : make_uint4(0, 0, 0, 0);
+      wsv[i] = v ? (uint32_t)*reinterpret_cast<const uint16_t*>(sr + k / 16) : 0u;
+    }
+  };
+  load_round(ks);
+
+  // 2. per-row power-of-two normalization of the activation scales
+  for (int b = wave; b < B; b += kSkThreads / 64) {
+    float m = 0.0f;
+    for (int64_t j = lane; j < kb16; j += 64) m = __builtin_fmaxf(m, a_scale[(int64_t)b * kb16 + j]);
+    m = wave_max(m);
+    if (lane == 0) {
+      const int e = row_exponent(m);
+      rs[b] = __builtin_ldexpf(1.0f, e);
+      rinv[b] = __builtin_ldexpf(1.0f, -e);
+    }
+  }
+  __syncthreads();
+
+  // 3. activations -> FP16 in LDS, eight codes per item
+  const int per_row = K / 8;
+  for (int idx = tid; idx < B * per_row; idx += kSkThreads) {
+    const int b = idx / per_row, q8 = idx - b * per_row;
+    const uint32_t codes = load_u32_bytes(a + (int64_t)b * kb2 + 4 * (int64_t)q8);
+    const float c = a_scale[(int64_t)b * kb16 + q8 / 2] * rinv[b];
+    *reinterpret_cast<v8h*>(As + (int64_t)b * pitch + 8 * q8) = dequant8_act(codes, c);
+  }
+  __syncthreads();
+
+  // 4. stream the weights
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  const bool bvalid = r16 < B;
+  const _Float16* arow = As + (bvalid ? r16 : 0) * pitch;
+  const v8h zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int c0 = ks;; ) {
+#pragma unroll
+    for (int i = 0; i < kSkPF; ++i) {
+      const int c = c0 + i * kSkKs;
+      if (c < nchunks) {
+        const int k = c * 128 + 32 * g;
+        const bool kv = k < K;
+        const _Float16 s0 = e4m3_b0_f16(wsv[i]), s1 = e4m3_b1_f16(wsv[i]);
+        const uint32_t cw[4] = {wc[i].x, wc[i].y, wc[i].z, wc[i].w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const v8h af = dequant8_f16(cw[m], m < 2 ? s0 : s1);
+          const v8h bf = (bvalid && kv) ? *reinterpret_cast<const v8h*>(arow + k + 8 * m) : zero8;
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, acc, 0, 0, 0);
+        }
+      }
+    }
+    c0 += kSkPF * kSkKs;
+    if (c0 >= nchunks) break;
+    load_round(c0);
+  }
+
+  // 5. sum the K quarters in a fixed order, scale, round to FP16
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[(ks * kSkRows + nsub * 16 + 4 * g + r) * 16 + r16] = acc[r];
+  __syncthreads();
+  const float gw = *w_g;
+  for (int t = tid; t < 16 * kSkRows; t += kSkThreads) {
+    const int b = t / kSkRows, nl = t % kSkRows;
+    const int n = blockIdx.x * kSkRows + nl;
+    if (b < B && n < N) {
+      float s = red[(0 * kSkRows + nl) * 16 + b];
+#pragma unroll
+      for (int q = 1; q < kSkKs; ++q) s += red[(q * kSkRows + nl) * 16 + b];
+      y[(int64_t)b * N + n] = (_Float16)((s * rs[b]) * gw);
+    }
+  }
+}
+
+// ------------------------------------------------------------ tiled (prefill)
+
+// Prologue: one workgroup per activation row -> normalized FP16 row and its
+// power of two.
+__global__ void __launch_bounds__(256)
+a_to_f16_rows(const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
+              _Float16* __restrict__ a16, float* __restrict__ rowscale, int K) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const int64_t kb16 = K / 16;
+  const float* sc = a_scale + row * kb16;
+  float m = 0.0f;
+  for (int64_t j = threadIdx.x; j < kb16; j += 256) m = __builtin_fmaxf(m, sc[j]);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+  const int e = row_exponent(m);
+  const float inv = __builtin_ldexpf(1.0f, -e);
+  if (threadIdx.x == 0) rowscale[row] = __builtin_ldexpf(1.0f, e);
+  const uint8_t* ar = a + row * (K / 2);
+  _Float16* out = a16 + row * K;
+  for (int64_t j = threadIdx.x; j < kb16; j += 256) {
+    const float c = sc[j] * inv;
+    const uint32_t c0 = load_u32_bytes(ar + 8 * j), c1 = load_u32_bytes(ar + 8 * j + 4);
+    *reinterpret_cast<v8h*>(out + 16 * j) = dequant8_act(c0, c);
+    *reinterpret_cast<v8h*>(out + 16 * j + 8) = dequant8_act(c1, c);
+  }
+}
+
+constexpr int kTM = 256, kTN = 256, kTK = 64;
+constexpr int kTThreads = 256;
+constexpr int kAStride = kTM + 1;                 // 16-byte rows per A column chunk (+1 pad)
+constexpr int kWStride = kTN + 1;
+constexpr size_t kAStage = (size_t)8 * kAStride * 16;
+constexpr size_t kWStage = (size_t)2 * kWStride * 16;
+constexpr size_t kSStage = (size_t)kTN * 4;
+constexpr size_t kStage = kAStage + kWStage + kSStage;
+constexpr size_t kTiledLds = 2 * kStage;
+
+__global__ void __launch_bounds__(kTThreads)
+gemm_tiled(const _Float16* __restrict__ a16, const float* __restrict__ rowscale,
+           const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_sf,
+           const float* __restrict__ w_g, _Float16* __restrict__ y, int B, int N, int K,
+           int tiles_n) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int tile = blockIdx.x;
+  const int tm = tile / tiles_n, tn = tile % tiles_n;
+  const int m0 = tm * kTM, n0 = tn * kTN;
+  const int64_t kb2 = K / 2, kb16 = K / 16;
+  const int nsteps = (K + kTK - 1) / kTK;
+
+  uint4 ra[8], rw[2];
+  uint32_t rsf;
+  auto gload = [&](int s) {
+    const int k0 = s * kTK;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int p = tid + kTThreads * i;
+      const int row = p >> 3, c = p & 7;
+      const int gr = m0 + row, k = k0 + 8 * c;
+      ra[i] = (gr < B && k < K) ? *reinterpret_cast<const uint4*>(a16 + (int64_t)gr * K + k)
+                                : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int p = tid + kTThreads * i;
+      const int row = p >> 1, hh = p & 1;
+      const int gn = n0 + row, k = k0 + 32 * hh;
+      rw[i] = (gn < N && k < K) ? *reinterpret_cast<const uint4*>(w + (int64_t)gn * kb2 + k / 2)
+                                : make_uint4(0, 0, 0, 0);
+    }
+    {
+      const int gn = n0 + tid;
+      uint32_t v = 0;
+      if (gn < N) {
+        const uint8_t* p = w_sf + (int64_t)gn * kb16 + k0 / 16;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (k0 + 16 * j < K) v |= (uint32_t)p[j] << (8 * j);
+      }
+      rsf = v;
+    }
+  };
+  auto lstore = [&](int buf) {
+    unsigned char* st = smem + buf * kStage;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int p = tid + kTThreads * i;
+      const int row = p >> 3, c = p & 7;
+      *reinterpret_cast<uint4*>(st + ((size_t)c * kAStride + row) * 16) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int p = tid + kTThreads * i;
+      const int row = p >> 1, hh = p & 1;
+      *reinterpret_cast<uint4*>(st + kAStage + ((size_t)hh * kWStride + row) * 16) = rw[i];
+    }
+    *reinterpret_cast<uint32_t*>(st + kAStage + kWStage + (size_t)tid * 4) = rsf;
+  };
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < nsteps) gload(s + 1);
+    const unsigned char* st = smem + buf * kStage;
+    uint4 wcode[4];
+    _Float16 wsc0[4], wsc1[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int nl = wn * 128 + nt * 32 + l32;
+      wcode[nt] = *reinterpret_cast<const uint4*>(st + kAStage + ((size_t)h * kWStride + nl) * 16);
+      // this lane group's two blocks are bytes 2h and 2h+1 of the row's scale word
+      const uint32_t sw = *reinterpret_cast<const uint32_t*>(st + kAStage + kWStage + (size_t)nl * 4) >> (16 * h);
+      wsc0[nt] = e4m3_b0_f16(sw);
+      wsc1[nt] = e4m3_b1_f16(sw);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      v8h af[4], bf[4];
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt) {
+        const int rl = wm * 128 + bt * 32 + l32;
+        af[bt] = *reinterpret_cast<const v8h*>(st + ((size_t)(4 * h + m) * kAStride + rl) * 16);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const uint32_t cw = (m == 0) ? wcode[nt].x : (m == 1) ? wcode[nt].y : (m == 2) ? wcode[nt].z : wcode[nt].w;
+        bf[nt] = dequant8_f16(cw, m < 2 ? wsc0[nt] : wsc1[nt]);
+      }
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          acc[bt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[bt], bf[nt], acc[bt][nt], 0, 0, 0);
+    }
+    if (s + 1 < nsteps) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float gw = *w_g;
+#pragma unroll
+  for (int bt = 0; bt < 4; ++bt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + wm * 128 + bt * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+      if (row >= B) continue;
+      const float rsc = rowscale[row] * gw;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int col = n0 + wn * 128 + nt * 32 + l32;
+        if (col < N) y[(int64_t)row * N + col] = (_Float16)(acc[bt][nt][r] * rsc);
+      }
+    }
+  }
+}
+
+// Dynamic LDS budget of the skinny kernel (its static LDS is 128 bytes).
+constexpr size_t kSkinnyDynMax = kMaxLds - 1024;
+
+bool use_skinny(int64_t B, int64_t K) { return B <= 16 && skinny_lds_bytes(B, K) <= kSkinnyDynMax; }
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+size_t gemm_workspace_bytes(int64_t B, int64_t N, int64_t K) {
+  (void)N;
+  if (use_skinny(B, K)) return 0;
+  return align256((size_t)B * (size_t)K * 2) + align256((size_t)B * 4);
+}
+
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, []() {
+    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_skinny),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSkinnyDynMax);
+    if (attr_err == hipSuccess)
+      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTiledLds);
+  });
+  if (attr_err != hipSuccess) return attr_err;
+  const int B = (int)g.B, N = (int)g.N, K = (int)g.K;
+  _Float16* y = reinterpret_cast<_Float16*>(g.y);
+  if (use_skinny(g.B, g.K)) {
+    const unsigned grid = (unsigned)((N + kSkRows - 1) / kSkRows);
+    hipLaunchKernelGGL(gemm_skinny, dim3(grid), dim3(kSkThreads), skinny_lds_bytes(B, K), s, g.a,
+                       g.a_scale, g.w, g.w_sf, g.w_g, y, B, N, K);
+    return hipGetLastError();
+  }
+  _Float16* a16 = reinterpret_cast<_Float16*>(g.workspace);
+  float* rowscale = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(g.workspace) +
+                                             align256((size_t)B * (size_t)K * 2));
+  hipLaunchKernelGGL(a_to_f16_rows, dim3((unsigned)B), dim3(256), 0, s, g.a, g.a_scale, a16,
+                     rowscale, K);
+  const int tiles_m = (B + kTM - 1) / kTM, tiles_n = (N + kTN - 1) / kTN;
+  hipLaunchKernelGGL(gemm_tiled, dim3((unsigned)(tiles_m * tiles_n)), dim3(kTThreads), kTiledLds,
+                     s, a16, rowscale, g.w, g.w_sf, g.w_g, y, B, N, K, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

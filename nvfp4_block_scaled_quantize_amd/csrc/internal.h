@@ -1,0 +1,71 @@
+// internal.h -- launcher interfaces between the C ABI layer and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+constexpr int kBf16 = 0;
+constexpr int kFp16 = 1;
+constexpr int kActNone = 0;
+constexpr int kActSwiglu = 1;
+constexpr int kActRelu2 = 2;
+
+struct QuantArgs {
+  const void* x;
+  int dtype;
+  int act;
+  int64_t rows;
+  int64_t k_out;       // quantized row length (input row is 2*k_out for SwiGLU)
+  int64_t group_rows;  // rows sharing one global scale
+  uint8_t* codes;
+  uint8_t* sf;
+  float* g_dec;
+  float* scale_out;    // may be null
+  float* parts;        // workspace: [groups, nparts] partial maxima (group_rows > 1)
+  int nparts;
+};
+
+// Number of partial maxima per group the per-group path uses.
+int quant_num_parts(int64_t group_elems);
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
+
+struct GemmArgs {
+  const uint8_t* a;
+  const float* a_scale;
+  const uint8_t* w;
+  const uint8_t* w_sf;
+  const float* w_g;
+  void* y;
+  int64_t B, N, K;
+  void* workspace;
+  size_t workspace_bytes;
+};
+
+size_t gemm_workspace_bytes(int64_t B, int64_t N, int64_t K);
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
+
+struct MoeArgs {
+  const float* logits;
+  const float* bias;
+  const void* x;
+  const uint8_t* w1;
+  const uint8_t* w1_sf;
+  const float* w1_g;
+  const uint8_t* w2;
+  const uint8_t* w2_sf;
+  const float* w2_g;
+  void* out;
+  int32_t* ids_out;
+  float* w_out;
+  int tokens, experts, top_k, hidden, inter, n_group, topk_group, norm;
+  float scaling;
+  void* workspace;
+  size_t workspace_bytes;
+};
+
+size_t moe_workspace_bytes(int tokens, int experts, int top_k, int hidden, int inter);
+hipError_t launch_moe(const MoeArgs& m, hipStream_t s);
+
+}  // namespace nvfp4

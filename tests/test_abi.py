@@ -1,0 +1,84 @@
+"""The C-ABI library loads and exports every function include/nvfp4_mi355x.h
+declares; host-side validation rejects bad arguments before touching a GPU.
+
+Runs without a GPU: only calls whose arguments fail validation are made (they
+return before any HIP call).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4_mi355x.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import nvfp4_block_scaled_quantize_amd as nv
+    return nv
+
+
+def test_every_declared_symbol_is_exported(nv):
+    names = _declared()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(nv.lib(), n), n
+    assert sorted(nv.EXPORTS) == names
+
+
+def test_status_strings(nv):
+    for s in range(5):
+        assert nv.lib().nvfp4_status_string(s)
+    assert nv.lib().nvfp4_status_string(99) == b"unknown status"
+
+
+def test_quantize_validation_without_gpu(nv):
+    L = nv.lib()
+    p = ctypes.c_void_p(256)   # never dereferenced: validation fails first
+    # K not a multiple of 16
+    assert L.nvfp4_quantize(p, 0, 4, 24, 1, p, p, p, None, None, 0, None) == nv.NVFP4_EINVAL
+    # bad dtype, bad group
+    assert L.nvfp4_quantize(p, 7, 4, 32, 1, p, p, p, None, None, 0, None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_quantize(p, 0, 6, 32, 4, p, p, p, None, None, 0, None) == nv.NVFP4_EINVAL
+    # null pointer
+    assert L.nvfp4_quantize(None, 0, 4, 32, 1, p, p, p, None, None, 0, None) == nv.NVFP4_EINVAL
+    # per-tensor without workspace
+    assert L.nvfp4_quantize(p, 0, 4, 32, 4, p, p, p, None, None, 0, None) == nv.NVFP4_EWORKSPACE
+    # rows == 0 is a no-op
+    assert L.nvfp4_quantize(p, 0, 0, 32, 1, p, p, p, None, None, 0, None) == nv.NVFP4_OK
+    # bad activation
+    assert L.nvfp4_act_quant(p, 0, 4, 32, 9, p, p, p, None, None) == nv.NVFP4_EINVAL
+    assert nv.lib().nvfp4_quantize_workspace_size(8, 64, 1) == 0
+    assert nv.lib().nvfp4_quantize_workspace_size(8, 64, 8) > 0
+
+
+def test_gemm_validation_without_gpu(nv):
+    L = nv.lib()
+    p = ctypes.c_void_p(256)
+    assert L.nvfp4_gemm(p, p, p, p, p, p, 4, 8, 48, None, 0, None) == nv.NVFP4_EINVAL   # K % 32
+    assert L.nvfp4_gemm(None, p, p, p, p, p, 4, 8, 64, None, 0, None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_gemm(p, p, ctypes.c_void_p(264), p, p, p, 4, 8, 64, None, 0, None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_gemm(p, p, p, p, p, p, 0, 8, 64, None, 0, None) == nv.NVFP4_OK
+    # large batches need a workspace
+    assert nv.gemm_workspace_size(4096, 8192, 8192) > 0
+    assert L.nvfp4_gemm(p, p, p, p, p, p, 4096, 8192, 8192, None, 0, None) == nv.NVFP4_EWORKSPACE
+
+
+def test_moe_validation_without_gpu(nv):
+    L = nv.lib()
+    p = ctypes.c_void_p(256)
+    args = [p] * 10 + [None, None]
+    # experts not divisible by n_group
+    assert L.nvfp4_moe_w4a16(*args, 4, 10, 2, 64, 64, 3, 1, 1, 1.0, None, 0, None) == nv.NVFP4_EINVAL
+    # top_k larger than the kept experts
+    assert L.nvfp4_moe_w4a16(*args, 4, 8, 5, 64, 64, 4, 2, 1, 1.0, None, 0, None) == nv.NVFP4_EINVAL
+    # missing workspace
+    assert L.nvfp4_moe_w4a16(*args, 4, 8, 2, 64, 64, 4, 2, 1, 1.0, None, 0, None) == nv.NVFP4_EWORKSPACE

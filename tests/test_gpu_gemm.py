@@ -1,0 +1,118 @@
+"""GPU parity of nvfp4_gemm against the fp64 oracle on the same quantized
+operands: relative Frobenius error <= 1e-3 (the operands are bit-identical;
+the only differences are the FP16 rounding of the activation operand, fp32
+accumulation order and the FP16 output rounding).
+
+Operand contract: "Fused Nvfp4 GEMM All Reduce Plugin", Baked-weight inputs
+(activation FP4 [B,K], activation_scale FP32 [B,1,K/16], weight FP4 [N,K],
+weight FP8 [N,K/16], scalar FP32 global) and Output (FP16 [B,N]).  Operands are
+produced by the oracle quantizer from seeded bf16 data (activations ~N(0,1)
+per token, weights ~N(0,0.02) per tensor), never by the GPU path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth_inputs as si
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import nvfp4_block_scaled_quantize_amd as nv
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return nv
+
+
+def _operands(oracle, a, w):
+    qa = oracle.quantize(a)
+    qw = oracle.quantize(w, group_rows=w.shape[0])
+    return qa, qw
+
+
+def _run(nv, qa, qw, **kw):
+    y = nv.gemm(torch.from_numpy(qa["codes"]).cuda(), torch.from_numpy(qa["scale"]).cuda(),
+                torch.from_numpy(qw["codes"]).cuda(), torch.from_numpy(qw["sf"]).cuda(),
+                torch.from_numpy(qw["g_dec"][:1]).cuda(), **kw)
+    torch.cuda.synchronize()
+    return y.cpu().double().numpy()
+
+
+def _ref(oracle, qa, qw, rows=None):
+    return oracle.gemm_ref(qa["codes"], qa["scale"], qw["codes"], qw["sf"], qw["g_dec"][0], rows=rows)
+
+
+@pytest.mark.parametrize("B,N,K", [(16, 256, 256),                      # quantize + GEMM workload
+                                   (1, 96, 32), (5, 100, 160), (3, 33, 4096 + 32),
+                                   (16, 64, 2048), (17, 64, 64), (37, 300, 96), (64, 512, 1024),
+                                   (300, 260, 544)])
+def test_small_shapes(nv, oracle, B, N, K):
+    a = si.bf16_normal((B, K), 1.0, 80, 0, seed=B + N + K)
+    w = si.bf16_normal((N, K), 0.02, 80, 1, seed=B + N + K)
+    qa, qw = _operands(oracle, a, w)
+    y = _run(nv, qa, qw)
+    ref = _ref(oracle, qa, qw)
+    err = oracle.rel_fro(y, ref)
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("B", [1, 4, 8])
+def test_decode_full_size(nv, oracle, B):
+    c = si.CONFIGS["C2"]
+    a, w = si.gemm_inputs("C2", B=B)
+    qa, qw = _operands(oracle, a, w)
+    y = _run(nv, qa, qw)
+    ref = _ref(oracle, qa, qw)
+    err = oracle.rel_fro(y, ref)
+    assert y.shape == (B, c["N"])
+    assert err <= TOL, err
+
+
+@pytest.fixture(scope="module")
+def prefill_operands(oracle):
+    a, w = si.gemm_inputs("C3")
+    return _operands(oracle, a, w)
+
+
+def test_prefill_full_size_sampled_rows(nv, oracle, prefill_operands):
+    qa, qw = prefill_operands
+    y = _run(nv, qa, qw)
+    rows = [0, 1, 255, 256, 1000, 2047, 3071, 4095]
+    ref = _ref(oracle, qa, qw, rows=rows)
+    err = oracle.rel_fro(y[rows], ref)
+    assert err <= TOL, err
+    assert np.all(np.isfinite(y))
+
+
+def test_identity_weights_return_activations(nv, oracle):
+    B, K = 24, 128
+    a = si.bf16_normal((B, K), 1.0, 81, 0)
+    qa = oracle.quantize(a)
+    nib = np.where(np.eye(K) > 0, 2, 0).astype(np.uint8)          # code 2 = 1.0
+    qw = {"codes": (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8),
+          "sf": np.full((K, K // 16), 0x38, np.uint8),                # E4M3 1.0
+          "g_dec": np.ones(1, np.float32)}
+    y = _run(nv, qa, qw)
+    A = oracle.dequant_act(qa["codes"], qa["scale"])
+    assert np.allclose(y, A, rtol=2e-3, atol=1e-6)
+
+
+def test_zero_activations_and_workspace_reuse(nv, oracle):
+    B, N, K = 40, 64, 256
+    a = torch.zeros((B, K), dtype=torch.bfloat16)
+    w = si.bf16_normal((N, K), 0.02, 82, 1)
+    qa, qw = _operands(oracle, a, w)
+    ws = torch.empty(nv.gemm_workspace_size(B, N, K), dtype=torch.uint8, device="cuda")
+    y = _run(nv, qa, qw, workspace=ws)
+    assert np.all(y == 0)
+
+
+def test_deterministic(nv, oracle):
+    a, w = si.gemm_inputs("C1")
+    qa, qw = _operands(oracle, a, w)
+    y1 = _run(nv, qa, qw)
+    y2 = _run(nv, qa, qw)
+    assert np.array_equal(y1, y2)
