@@ -1,0 +1,318 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 hot path on one MI355X.
+
+A step is one pass of the path over one batch: per-token NVFP4 quantization
+of the activations (nvfp4_act_quant) followed by the block-scaled NVFP4 GEMM
+(nvfp4_gemm) against pre-quantized weights.  The headline workload is the
+prefill GEMM B=4096, K=8192, N=8192 (bf16 activations ~N(0,1), weights
+~N(0,0.02) quantized per tensor, FP16 output); `value` is whole-step TFLOP/s
+(2*B*N*K per step).  The other workloads (decode GEMM, fused SwiGLU quantize,
+quantize + GEMM small case, MoE) are measured after it and reported under
+"workloads".
+
+Timing: inputs are resident in HBM before the timed region; W warmup steps,
+then exactly K steps between synchronizations, timed with HIP events on the
+stream the kernels run on; per-call events give the average duration of the
+GEMM call and of the quantize call.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP16_MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 MFMA
+FP4_MFMA_PEAK_TFLOPS = 10100.0  # dense fp4 MFMA (context: the path runs fp16 MFMA)
+ALGO_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--quick", action="store_true", help="skip the secondary workloads and the CPU baseline")
+    p.add_argument("--no-cpu", action="store_true")
+    return p.parse_args()
+
+
+class EventTimer:
+    """Average duration of a repeated call, measured with HIP events on `stream`."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream, self.pairs = torch, stream, []
+
+    def __call__(self, fn):
+        t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record(self.stream)
+        r = fn()
+        b.record(self.stream)
+        self.pairs.append((a, b))
+        return r
+
+    def mean_ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(len(self.pairs), 1)
+
+
+def quant_bytes(rows, k_in, k_out, scale=True):
+    """Algorithmic HBM bytes of one quantize call: read input, write codes,
+    E4M3 bytes, the FP32 global per row and (optionally) the combined scales."""
+    return rows * k_in * 2 + rows * k_out // 2 + rows * k_out // 16 + rows * 4 + (rows * k_out // 16 * 4 if scale else 0)
+
+
+def gemm_bytes(B, N, K):
+    """Algorithmic bytes of one GEMM call: each operand read once, output written once."""
+    return B * K // 2 + B * (K // 16) * 4 + N * K // 2 + N * (K // 16) + 4 + B * N * 2
+
+
+def run_prefill(torch, nv, si, steps, warmup):
+    c = si.CONFIGS["C3"]
+    B, K, N = c["B"], c["K"], c["N"]
+    dev = torch.device("cuda:0")
+    a, w = si.gemm_inputs("C3")
+    x = a.to(dev)
+    wq = nv.quantize(w.to(dev), group_rows=N, want_scale=False)
+    del w
+    stream = torch.cuda.current_stream()
+    qa = {"codes": torch.empty((B, K // 2), dtype=torch.uint8, device=dev),
+          "sf": torch.empty((B, K // 16), dtype=torch.uint8, device=dev),
+          "g_dec": torch.empty((B,), dtype=torch.float32, device=dev),
+          "scale": torch.empty((B, K // 16), dtype=torch.float32, device=dev)}
+    y = torch.empty((B, N), dtype=torch.float16, device=dev)
+    ws = torch.empty(max(nv.gemm_workspace_size(B, N, K), 1), dtype=torch.uint8, device=dev)
+
+    def step(tq=None, tg=None):
+        fq = lambda: nv.act_quant(x, "none", out=qa)
+        fg = lambda: nv.gemm(qa["codes"], qa["scale"], wq["codes"], wq["sf"], wq["g_dec"], out=y, workspace=ws)
+        tq(fq) if tq else fq()
+        tg(fg) if tg else fg()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    tq, tg = EventTimer(torch, stream), EventTimer(torch, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step(tq, tg)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / steps
+    return dict(B=B, K=K, N=N, ms_step=ms_step, wall_s=wall, ms_gemm=tg.mean_ms(), ms_quant=tq.mean_ms(),
+                flops=2.0 * B * N * K, qbytes=quant_bytes(B, K, K), gbytes=gemm_bytes(B, N, K))
+
+
+def run_decode(torch, nv, si, B, iters=50):
+    """Decode GEMM (one rank's K-share) with the weights rotated through > 512 MB
+    so the 256 MB Infinity Cache cannot hold them."""
+    c = si.CONFIGS["C2"]
+    K, N = c["K"], c["N"]
+    dev = torch.device("cuda:0")
+    a, w = si.gemm_inputs("C2", B=B)
+    wq = nv.quantize(w.to(dev), group_rows=N, want_scale=False)
+    copies = 32
+    Ws = [(wq["codes"].clone(), wq["sf"].clone(), wq["g_dec"].clone()) for _ in range(copies)]
+    x = a.to(dev)
+    qa = nv.act_quant(x, "none")
+    y = torch.empty((B, N), dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream()
+    for i in range(copies):
+        nv.gemm(qa["codes"], qa["scale"], *Ws[i], out=y)
+    torch.cuda.synchronize()
+    tg, tq = EventTimer(torch, stream), EventTimer(torch, stream)
+    for i in range(iters):
+        tq(lambda: nv.act_quant(x, "none", out=qa))
+        Wi = Ws[i % copies]
+        tg(lambda: nv.gemm(qa["codes"], qa["scale"], *Wi, out=y))
+    torch.cuda.synchronize()
+    gb = gemm_bytes(B, N, K)
+    return dict(B=B, us_gemm=tg.mean_ms() * 1e3, us_quant=tq.mean_ms() * 1e3, gemm_bytes=gb,
+                gemm_GBps=gb / (tg.mean_ms() * 1e-3) / 1e9,
+                hbm_frac=gb / (tg.mean_ms() * 1e-3) / 1e9 / HBM_PEAK_GBS)
+
+
+def run_swiglu(torch, nv, si, iters=20):
+    c = si.CONFIGS["C4"]
+    rows, H = c["rows"], c["H"]
+    dev = torch.device("cuda:0")
+    x = si.swiglu_input().to(dev)
+    out = nv.act_quant(x, "swiglu", want_scale=False)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        nv.act_quant(x, "swiglu", out=out)
+    torch.cuda.synchronize()
+    t = EventTimer(torch, stream)
+    for _ in range(iters):
+        t(lambda: nv.act_quant(x, "swiglu", out=out))
+    torch.cuda.synchronize()
+    by = quant_bytes(rows, 2 * H, H, scale=False)
+    return dict(rows=rows, H=H, us=t.mean_ms() * 1e3, bytes=by, GBps=by / (t.mean_ms() * 1e-3) / 1e9,
+                hbm_frac=by / (t.mean_ms() * 1e-3) / 1e9 / HBM_PEAK_GBS)
+
+
+def run_small(torch, nv, si, iters=50):
+    c = si.CONFIGS["C1"]
+    B, K, N = c["B"], c["K"], c["N"]
+    dev = torch.device("cuda:0")
+    a, w = si.gemm_inputs("C1")
+    x = a.to(dev)
+    wq = nv.quantize(w.to(dev), group_rows=N, want_scale=False)
+    qa = nv.act_quant(x, "none")
+    y = nv.gemm(qa["codes"], qa["scale"], wq["codes"], wq["sf"], wq["g_dec"])
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        nv.act_quant(x, "none", out=qa)
+        nv.gemm(qa["codes"], qa["scale"], wq["codes"], wq["sf"], wq["g_dec"], out=y)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return dict(B=B, K=K, N=N, us_step=e0.elapsed_time(e1) / iters * 1e3)
+
+
+def run_moe(torch, nv, si, iters=20):
+    c = si.CONFIGS["C5"]
+    dev = torch.device("cuda:0")
+    d = si.moe_inputs()
+    T, E, Hd, I = d["T"], d["E"], d["hidden"], d["inter"]
+    w1 = nv.quantize(d["w1"].to(dev), group_rows=I, want_scale=False)
+    w2 = nv.quantize(d["w2"].to(dev), group_rows=Hd, want_scale=False)
+    args = [torch.from_numpy(d["logits"]).to(dev), torch.from_numpy(d["bias"]).to(dev), d["x"].to(dev),
+            w1["codes"].view(E, I, Hd // 2), w1["sf"].view(E, I, Hd // 16), w1["g_dec"],
+            w2["codes"].view(E, Hd, I // 2), w2["sf"].view(E, Hd, I // 16), w2["g_dec"]]
+    copies = 4
+    sets = [args] + [[t.clone() if i >= 3 else t for i, t in enumerate(args)] for _ in range(copies - 1)]
+    out = torch.empty((T, Hd), dtype=torch.float16, device=dev)
+    ws = torch.empty(nv.moe_workspace_size(T, E, c["top_k"], Hd, I), dtype=torch.uint8, device=dev)
+    kw = dict(top_k=c["top_k"], n_group=c["n_group"], topk_group=c["topk_group"],
+              norm_topk_prob=c["norm_topk_prob"], routed_scaling=c["routed_scaling"], out=out, workspace=ws)
+    for s in sets:
+        nv.moe_w4a16(*s, **kw)
+    torch.cuda.synchronize()
+    t = EventTimer(torch, torch.cuda.current_stream())
+    for i in range(iters):
+        s = sets[i % copies]
+        t(lambda: nv.moe_w4a16(*s, **kw))
+    torch.cuda.synchronize()
+    wbytes = E * (I * Hd // 2 + I * Hd // 16 + Hd * I // 2 + Hd * I // 16) + 2 * E * 4
+    by = wbytes + T * Hd * 2 * 2 + T * E * 4 + E * 4
+    return dict(T=T, E=E, us=t.mean_ms() * 1e3, bytes=by, GBps=by / (t.mean_ms() * 1e-3) / 1e9,
+                hbm_frac=by / (t.mean_ms() * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                flops=2.0 * T * c["top_k"] * (2 * Hd * I))
+
+
+def cpu_baseline(si, pre):
+    """The oracle as it stands on a bounded sample of the prefill step: per-token
+    quantization of R activation rows (C oracle, one thread) and the fp64 GEMM
+    reference for those rows against the full weight matrix (numpy BLAS)."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+    R = 16
+    c = si.CONFIGS["C3"]
+    K, N = c["K"], c["N"]
+    a, w = si.gemm_inputs("C3")
+    wq = oracle.quantize(w, group_rows=N, want_scale=False)    # offline weight prep: not timed
+    rows = a[:R]
+    t0 = time.perf_counter()
+    qa = oracle.quantize(rows)
+    oracle.gemm_ref(qa["codes"], qa["scale"], wq["codes"], wq["sf"], wq["g_dec"][0])
+    dt = time.perf_counter() - t0
+    blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    cores = max(blas) if blas else 1
+    return {"value": 2.0 * R * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "%d of %d activation rows: C-oracle per-token quantize (1 thread) + fp64 numpy GEMM "
+                      "reference against the full %dx%d weight (%.1f s)" % (R, c["B"], N, K, dt)}
+
+
+def load_traffic(name):
+    try:
+        with open(ALGO_TRAFFIC_FILE) as f:
+            return json.load(f).get(name)
+    except (OSError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the NVFP4 path here is a single-GPU build "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import nvfp4_block_scaled_quantize_amd as nv
+    import synth_inputs as si
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    log("prefill: act_quant [4096,8192] + gemm 4096x8192x8192, %d warmup + %d steps" % (args.warmup, args.steps))
+    pre = run_prefill(torch, nv, si, args.steps, args.warmup)
+    value = pre["flops"] / (pre["ms_step"] * 1e-3) / 1e12
+    gemm_tflops = pre["flops"] / (pre["ms_gemm"] * 1e-3) / 1e12
+    quant_gbs = pre["qbytes"] / (pre["ms_quant"] * 1e-3) / 1e9
+    log("prefill step %.3f ms (gemm %.3f ms = %.1f TFLOP/s, quant %.3f ms = %.0f GB/s)" % (
+        pre["ms_step"], pre["ms_gemm"], gemm_tflops, pre["ms_quant"], quant_gbs))
+    workloads = {"prefill_C3": {
+        "gemm_ms": round(pre["ms_gemm"], 4), "gemm_TFLOPs": round(gemm_tflops, 1),
+        "gemm_frac_fp16_peak": round(gemm_tflops / FP16_MFMA_PEAK_TFLOPS, 4),
+        "gemm_frac_fp4_peak": round(gemm_tflops / FP4_MFMA_PEAK_TFLOPS, 4),
+        "act_quant_ms": round(pre["ms_quant"], 4), "act_quant_GBps": round(quant_gbs, 1),
+        "act_quant_hbm_frac": round(quant_gbs / HBM_PEAK_GBS, 4)}}
+    if not args.quick:
+        for B in (1, 4, 8):
+            log("decode B=%d" % B)
+            workloads["decode_C2_B%d" % B] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                              for k, v in run_decode(torch, nv, si, B).items()}
+        log("swiglu quantize")
+        workloads["swiglu_quant_C4"] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                        for k, v in run_swiglu(torch, nv, si).items()}
+        log("small quantize + gemm")
+        workloads["small_C1"] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                 for k, v in run_small(torch, nv, si).items()}
+        try:
+            log("moe")
+            workloads["moe_C5"] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                   for k, v in run_moe(torch, nv, si).items()}
+        except Exception as e:  # reported, not hidden
+            workloads["moe_C5"] = {"error": str(e)[:200]}
+    cpu = None
+    if not args.quick and not args.no_cpu:
+        log("cpu baseline (oracle sample)")
+        cpu = cpu_baseline(si, pre)
+    line = {
+        "metric": "NVFP4 GEMM TFLOPS + quantize GB/s at 1 MI355X, % of FP4/HBM roofline",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(pre["ms_step"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
+        "data": "synthetic (seeded bf16 normals; weights quantized to NVFP4 on the GPU before timing)",
+        "config": {"workload": "prefill: per-token act quantize [4096,8192] + NVFP4 GEMM B=4096 K=8192 N=8192",
+                   "B": pre["B"], "K": pre["K"], "N": pre["N"], "parallelism": "single GPU"},
+        "roofline": {"kernel": "nvfp4_gemm (prefill)", "bound": "mfma", "achieved": round(gemm_tflops, 1),
+                     "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / FP16_MFMA_PEAK_TFLOPS, 4),
+                     "traffic": load_traffic("gemm_tiled")},
+        "cpu_baseline": cpu,
+        "workloads": workloads,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

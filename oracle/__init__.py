@@ -269,21 +269,24 @@ def moe_ref(x_fp16: np.ndarray, ids: np.ndarray, weights: np.ndarray,
 
     ("Nvfp4 A16 Blackwell Moe Runner": FP16 activations, NVFP4 fc1/fc2 weights
     with per-expert FP32 global scales, ReLU2.)  `tokens` restricts the rows.
+    Each expert's weights are dequantized once; the per-pair results are summed
+    per token in rank order j = 0..top_k-1.
     """
     x = np.asarray(x_fp16).astype(np.float64)
-    T = x.shape[0]
-    tok = range(T) if tokens is None else tokens
-    H = x.shape[1]
-    out = np.zeros((len(list(tok)), H), np.float64)
-    cache1, cache2 = {}, {}
+    tok = list(range(x.shape[0])) if tokens is None else list(tokens)
+    top_k = ids.shape[1]
+    o = {}
+    experts = sorted({int(ids[t, j]) for t in tok for j in range(top_k)})
+    for e in experts:
+        W1 = dequant_weight(w1_codes[e], w1_sf[e], w1_g[e])
+        W2 = dequant_weight(w2_codes[e], w2_sf[e], w2_g[e])
+        for t in tok:
+            for j in range(top_k):
+                if int(ids[t, j]) == e:
+                    h = np.maximum(W1 @ x[t], 0.0) ** 2
+                    o[(t, j)] = W2 @ h
+    out = np.zeros((len(tok), x.shape[1]), np.float64)
     for oi, t in enumerate(tok):
-        for j in range(ids.shape[1]):
-            e = int(ids[t, j])
-            if e not in cache1:
-                cache1[e] = dequant_weight(w1_codes[e], w1_sf[e], w1_g[e])
-                cache2[e] = dequant_weight(w2_codes[e], w2_sf[e], w2_g[e])
-            h = cache1[e] @ x[t]
-            h = np.maximum(h, 0.0) ** 2
-            o = cache2[e] @ h
-            out[oi] += float(weights[t, j]) * o
+        for j in range(top_k):
+            out[oi] += float(weights[t, j]) * o[(t, j)]
     return out

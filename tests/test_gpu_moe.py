@@ -1,0 +1,94 @@
+"""GPU parity of nvfp4_moe_w4a16 against the oracle.
+
+Routing ("Nvfp4 A16 Blackwell Moe Runner", Nvfp4A16BlackwellMoeParams:
+sigmoid group-top-k with correction bias, normTopkProb, routedScalingFactor):
+expert ids must equal the oracle's exactly and the weights bit-for-bit (both
+sides evaluate the same binary32 operations).  Layer output: relative
+Frobenius error <= 1e-3 against the fp64 oracle on the same NVFP4 weights
+(quantized per expert by the oracle) and the oracle's routing.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth_inputs as si
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import nvfp4_block_scaled_quantize_amd as nv
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return nv
+
+
+def _case(oracle, T, E, hidden, inter, seed, w_std=0.02):
+    logits = si.normal_f32((T, E), 1.0, 70, 3, seed)
+    bias = si.normal_f32((E,), 0.1, 70, 4, seed)
+    x = si.fp16_normal((T, hidden), 1.0, 70, 0, seed)
+    w1 = si.bf16_normal((E * inter, hidden), w_std, 70, 1, seed)
+    w2 = si.bf16_normal((E * hidden, inter), w_std, 70, 2, seed)
+    q1 = oracle.quantize(w1, group_rows=inter, want_scale=False)
+    q2 = oracle.quantize(w2, group_rows=hidden, want_scale=False)
+    return dict(logits=logits, bias=bias, x=x,
+                w1=(q1["codes"].reshape(E, inter, hidden // 2), q1["sf"].reshape(E, inter, hidden // 16), q1["g_dec"]),
+                w2=(q2["codes"].reshape(E, hidden, inter // 2), q2["sf"].reshape(E, hidden, inter // 16), q2["g_dec"]))
+
+
+def _run(nv, c, top_k, n_group, topk_group, norm=True, scaling=1.0):
+    dev = "cuda"
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    out, ids, wts = nv.moe_w4a16(t(c["logits"]), t(c["bias"]), c["x"].to(dev), t(c["w1"][0]), t(c["w1"][1]),
+                                 t(c["w1"][2]), t(c["w2"][0]), t(c["w2"][1]), t(c["w2"][2]), top_k=top_k,
+                                 n_group=n_group, topk_group=topk_group, norm_topk_prob=norm,
+                                 routed_scaling=scaling, want_routing=True)
+    torch.cuda.synchronize()
+    return out.cpu().double().numpy(), ids.cpu().numpy(), wts.cpu().numpy()
+
+
+def _check(oracle, nv, c, top_k, n_group, topk_group, norm=True, scaling=1.0, tokens=None):
+    out, ids, wts = _run(nv, c, top_k, n_group, topk_group, norm, scaling)
+    rid, rw = oracle.route(c["logits"], c["bias"], top_k, n_group, topk_group, norm, scaling)
+    assert np.array_equal(ids, rid)
+    assert np.array_equal(wts.view(np.uint32), rw.view(np.uint32))
+    ref = oracle.moe_ref(c["x"].numpy(), rid, rw, *c["w1"], *c["w2"], tokens=tokens)
+    got = out if tokens is None else out[tokens]
+    err = oracle.rel_fro(got, ref)
+    assert err <= TOL, err
+    assert np.all(np.isfinite(out))
+
+
+@pytest.mark.parametrize("T,E,top_k,n_group,topk_group,hidden,inter",
+                         [(5, 8, 2, 2, 1, 64, 96), (32, 16, 4, 4, 2, 256, 128), (70, 64, 8, 8, 4, 128, 64),
+                          (300, 32, 6, 4, 3, 96, 160), (3, 256, 16, 16, 4, 64, 64),
+                          (600, 8, 4, 2, 2, 64, 64)])
+def test_small_layers(nv, oracle, T, E, top_k, n_group, topk_group, hidden, inter):
+    c = _case(oracle, T, E, hidden, inter, seed=T + E)
+    _check(oracle, nv, c, top_k, n_group, topk_group)
+
+
+def test_no_normalisation_and_scaling(nv, oracle):
+    c = _case(oracle, 24, 16, 64, 64, seed=9)
+    _check(oracle, nv, c, 4, 4, 2, norm=False, scaling=2.5)
+
+
+def test_full_size_sampled_tokens(nv, oracle):
+    cf = si.CONFIGS["C5"]
+    d = si.moe_inputs()
+    E, H, I = d["E"], d["hidden"], d["inter"]
+    q1 = oracle.quantize(d["w1"], group_rows=I, want_scale=False)
+    q2 = oracle.quantize(d["w2"], group_rows=H, want_scale=False)
+    c = dict(logits=d["logits"], bias=d["bias"], x=d["x"],
+             w1=(q1["codes"].reshape(E, I, H // 2), q1["sf"].reshape(E, I, H // 16), q1["g_dec"]),
+             w2=(q2["codes"].reshape(E, H, I // 2), q2["sf"].reshape(E, H, I // 16), q2["g_dec"]))
+    _check(oracle, nv, c, cf["top_k"], cf["n_group"], cf["topk_group"], cf["norm_topk_prob"],
+           cf["routed_scaling"], tokens=[0, 1, 2, 100, 200, 255])
+
+
+def test_deterministic(nv, oracle):
+    c = _case(oracle, 40, 16, 128, 64, seed=11)
+    a = _run(nv, c, 4, 4, 2)[0]
+    b = _run(nv, c, 4, 4, 2)[0]
+    assert np.array_equal(a, b)
