@@ -378,6 +378,344 @@ gemm_tiled(const _Float16* __restrict__ a16, const float* __restrict__ rowscale,
 // Dynamic LDS budget of the skinny kernel (its static LDS is 128 bytes).
 constexpr size_t kSkinnyDynMax = kMaxLds - 1024;
 
+// ------------------------------------------------------------ tiled, LDS-DMA pipeline
+//
+// Same tile and arithmetic as gemm_tiled, with the operand movement rebuilt
+// for latency hiding: the FP16 activations, the FP4 weight codes and the
+// E4M3 bytes go straight from global memory into LDS with
+// global_load_lds_dwordx4 / _dword (no staging registers), three LDS stages
+// deep (two stages of loads in flight while one is consumed), one barrier per
+// 64-k stage, and the MFMA operands of the next k-substep are read and
+// dequantized while the current 16 MFMAs run.  Requires K % 64 == 0.
+
+#define NVFP4_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+constexpr int kPStages = 3;
+constexpr int kPAChunk = kTM * 16 + 64;          // one 8-k column of 256 rows (+64 B skew)
+constexpr int kPWHalf = kTN * 16 + 64;           // one 32-k half of 256 weight rows (+skew)
+constexpr int kPAOff = 0;
+constexpr int kPWOff = 8 * kPAChunk;
+constexpr int kPSOff = kPWOff + 2 * kPWHalf;
+constexpr int kPStage = kPSOff + kTN * 4;
+constexpr size_t kPipeLds = 0;   // all LDS of the pipelined kernel is static
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4]=7 | lgkmcnt[11:8]=15 | vmcnt[5:4] in bits [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 0xF) | ((N >> 4) << 14));
+}
+
+// LDS byte address of a shared-memory pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
+}
+
+// Direct global -> LDS copies of 16 (4) bytes per lane: lane i's bytes land at
+// LDS address lds + 16*i (4*i).  Written as inline assembly so that the
+// compiler does not treat every later LDS read as dependent on these
+// asynchronous writes (it would wait for all outstanding vector-memory
+// operations, including the loads of the stages in flight).  The kernel waits
+// for them itself with s_waitcnt vmcnt + s_barrier before reading a stage.
+// These instructions produce no VGPR result.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t vofs, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds), "v"(vofs), "s"(sbase) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t vofs, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(lds), "v"(vofs), "s"(sbase) : "memory", "m0");
+}
+
+__global__ void __launch_bounds__(kTThreads)
+gemm_tiled_pipe(const _Float16* __restrict__ a16, const float* __restrict__ rowscale,
+                const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_sf,
+                const float* __restrict__ w_g, _Float16* __restrict__ y, int B, int N, int K,
+                int tiles_m, int tiles_n) {
+  // Three stage buffers; the stage loop is unrolled by three so that every
+  // buffer is named statically.
+  __shared__ __attribute__((aligned(16))) unsigned char lds0[kPStage];
+  __shared__ __attribute__((aligned(16))) unsigned char lds1[kPStage];
+  __shared__ __attribute__((aligned(16))) unsigned char lds2[kPStage];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, h = lane >> 5;
+  // XCD-aware order: consecutive workgroup ids land on different XCDs, so
+  // give each XCD a contiguous run of tiles (it then shares A rows in its L2).
+  const int ntiles = tiles_m * tiles_n;
+  int tile = blockIdx.x;
+  if (ntiles % 8 == 0) tile = (tile % 8) * (ntiles / 8) + tile / 8;
+  const int tm = tile / tiles_n, tn = tile % tiles_n;
+  const int m0 = tm * kTM, n0 = tn * kTN;
+  const int nsteps = K / kTK;
+
+  // per-lane 32-bit byte offsets of this wave's DMA sources (rows clamped to
+  // the matrix; clamped rows only feed outputs that are never stored)
+  uint32_t aofs[8], wofs[2], sofs;
+  int alds[8], wlds[2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int i = wave * 8 + j, c = i >> 2, q = i & 3;
+    int r = m0 + 64 * q + lane;
+    r = r < B ? r : B - 1;
+    aofs[j] = (uint32_t)r * (uint32_t)K * 2u + 16u * c;
+    alds[j] = kPAOff + c * kPAChunk + q * 1024;
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = wave * 2 + j, hh = i >> 2, q = i & 3;
+    int r = n0 + 64 * q + lane;
+    r = r < N ? r : N - 1;
+    wofs[j] = (uint32_t)r * (uint32_t)(K / 2) + 16u * hh;
+    wlds[j] = kPWOff + hh * kPWHalf + q * 1024;
+  }
+  {
+    int r = n0 + 64 * wave + lane;
+    r = r < N ? r : N - 1;
+    sofs = (uint32_t)r * (uint32_t)(K / 16);
+  }
+  const int slds = kPSOff + wave * 256;
+  const unsigned char* abase = reinterpret_cast<const unsigned char*>(a16);
+
+  auto issue = [&](unsigned char* buf, int st) {
+    const int k0 = st * kTK;
+    const unsigned char* ab = abase + (size_t)k0 * 2;
+    const uint8_t* wb = w + k0 / 2;
+    const uint8_t* sb = w_sf + k0 / 16;
+    const uint32_t l0 = lds_addr(buf);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dma16(ab, aofs[j], l0 + alds[j]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16(wb, wofs[j], l0 + wlds[j]);
+    dma4(sb, sofs, l0 + slds);
+  };
+  constexpr int kLoadsPerStage = 11;
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  auto compute = [&](const unsigned char* st) {
+    uint4 wcode[4];
+    v2h wsc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int nl = wn * 128 + nt * 32 + l32;
+      wcode[nt] = *reinterpret_cast<const uint4*>(st + kPWOff + h * kPWHalf + nl * 16);
+      const uint32_t sw = *reinterpret_cast<const uint32_t*>(st + kPSOff + nl * 4) >> (16 * h);
+      wsc[nt][0] = e4m3_b0_f16(sw);
+      wsc[nt][1] = e4m3_b1_f16(sw);
+    }
+    v8h af[2][4], bf[2][4];
+    auto load_a = [&](int m, v8h* dst) {
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt) {
+        const int rl = wm * 128 + bt * 32 + l32;
+        dst[bt] = *reinterpret_cast<const v8h*>(st + kPAOff + (4 * h + m) * kPAChunk + rl * 16);
+      }
+    };
+    auto deq_w = [&](int m, v8h* dst) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const uint32_t cw = (m == 0) ? wcode[nt].x : (m == 1) ? wcode[nt].y : (m == 2) ? wcode[nt].z : wcode[nt].w;
+        dst[nt] = dequant8_f16(cw, wsc[nt][m >> 1]);
+      }
+    };
+    load_a(0, af[0]);
+    deq_w(0, bf[0]);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int cur = m & 1;
+      if (m < 3) {
+        // operands of the next k-substep, overlapped with this substep's MFMAs
+        load_a(m + 1, af[cur ^ 1]);
+        deq_w(m + 1, bf[cur ^ 1]);
+      }
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          acc[bt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][bt], bf[cur][nt], acc[bt][nt], 0, 0, 0);
+    }
+  };
+  // one 64-k stage: wait for its DMA, barrier, start stage s+2's DMA, compute
+  auto step = [&](const unsigned char* cur, unsigned char* next2, int s) {
+    if (s + 1 < nsteps) wait_vmcnt_le<kLoadsPerStage>();
+    else wait_vmcnt_le<0>();
+    __builtin_amdgcn_s_barrier();
+    if (s + 2 < nsteps) issue(next2, s + 2);
+    compute(cur);
+  };
+
+  issue(lds0, 0);
+  if (nsteps > 1) issue(lds1, 1);
+  for (int s = 0; s < nsteps; s += 3) {
+    step(lds0, lds2, s);
+    if (s + 1 < nsteps) step(lds1, lds0, s + 1);
+    if (s + 2 < nsteps) step(lds2, lds1, s + 2);
+  }
+
+  const float gw = *w_g;
+#pragma unroll
+  for (int bt = 0; bt < 4; ++bt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + wm * 128 + bt * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+      if (row >= B) continue;
+      const float rsc = rowscale[row] * gw;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int col = n0 + wn * 128 + nt * 32 + l32;
+        if (col < N) y[(int64_t)row * N + col] = (_Float16)(acc[bt][nt][r] * rsc);
+      }
+    }
+  }
+}
+
+// Eight-wave variant: the 256x256 tile is split into 2 x 4 wave tiles of
+// 128 x 64, so each wave holds 128 accumulators and two waves share a SIMD;
+// the hardware then overlaps one wave's LDS reads and dequantization with the
+// other wave's MFMAs.  Same LDS stages and DMA as gemm_tiled_pipe.
+constexpr int kP2Threads = 512;
+
+__global__ void __launch_bounds__(kP2Threads)
+gemm_tiled_pipe8(const _Float16* __restrict__ a16, const float* __restrict__ rowscale,
+                 const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_sf,
+                 const float* __restrict__ w_g, _Float16* __restrict__ y, int B, int N, int K,
+                 int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds0[kPStage];
+  __shared__ __attribute__((aligned(16))) unsigned char lds1[kPStage];
+  __shared__ __attribute__((aligned(16))) unsigned char lds2[kPStage];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;          // 2 x 4 waves of 128 x 64
+  const int l32 = lane & 31, h = lane >> 5;
+  const int ntiles = tiles_m * tiles_n;
+  int tile = blockIdx.x;
+  if (ntiles % 8 == 0) tile = (tile % 8) * (ntiles / 8) + tile / 8;
+  const int tm = tile / tiles_n, tn = tile % tiles_n;
+  const int m0 = tm * kTM, n0 = tn * kTN;
+  const int nsteps = K / kTK;
+
+  // DMA work of this wave per stage: 4 of the 32 A copies, 1 of the 8 W
+  // copies, and (waves 0..3) 1 of the 4 scale copies.
+  uint32_t aofs[4], wofs, sofs;
+  int alds[4], wlds, slds;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = wave * 4 + j, c = i >> 2, q = i & 3;
+    int r = m0 + 64 * q + lane;
+    r = r < B ? r : B - 1;
+    aofs[j] = (uint32_t)r * (uint32_t)K * 2u + 16u * c;
+    alds[j] = kPAOff + c * kPAChunk + q * 1024;
+  }
+  {
+    const int hh = wave >> 2, q = wave & 3;
+    int r = n0 + 64 * q + lane;
+    r = r < N ? r : N - 1;
+    wofs = (uint32_t)r * (uint32_t)(K / 2) + 16u * hh;
+    wlds = kPWOff + hh * kPWHalf + q * 1024;
+  }
+  const bool sdma = wave < 4;
+  {
+    int r = n0 + 64 * (wave & 3) + lane;
+    r = r < N ? r : N - 1;
+    sofs = (uint32_t)r * (uint32_t)(K / 16);
+    slds = kPSOff + (wave & 3) * 256;
+  }
+  const unsigned char* abase = reinterpret_cast<const unsigned char*>(a16);
+
+  auto issue = [&](unsigned char* buf, int st) {
+    const int k0 = st * kTK;
+    const unsigned char* ab = abase + (size_t)k0 * 2;
+    const uint32_t l0 = lds_addr(buf);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(ab, aofs[j], l0 + alds[j]);
+    dma16(w + k0 / 2, wofs, l0 + wlds);
+    if (sdma) dma4(w_sf + k0 / 16, sofs, l0 + slds);
+  };
+
+  v16f acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  auto compute = [&](const unsigned char* st) {
+    uint4 wcode[2];
+    v2h wsc[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int nl = wn * 64 + nt * 32 + l32;
+      wcode[nt] = *reinterpret_cast<const uint4*>(st + kPWOff + h * kPWHalf + nl * 16);
+      const uint32_t sw = *reinterpret_cast<const uint32_t*>(st + kPSOff + nl * 4) >> (16 * h);
+      wsc[nt][0] = e4m3_b0_f16(sw);
+      wsc[nt][1] = e4m3_b1_f16(sw);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      v8h af[4], bf[2];
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt) {
+        const int rl = wm * 128 + bt * 32 + l32;
+        af[bt] = *reinterpret_cast<const v8h*>(st + kPAOff + (4 * h + m) * kPAChunk + rl * 16);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const uint32_t cw = (m == 0) ? wcode[nt].x : (m == 1) ? wcode[nt].y : (m == 2) ? wcode[nt].z : wcode[nt].w;
+        bf[nt] = dequant8_f16(cw, wsc[nt][m >> 1]);
+      }
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          acc[bt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[bt], bf[nt], acc[bt][nt], 0, 0, 0);
+    }
+  };
+  auto step = [&](const unsigned char* cur, unsigned char* next2, int s) {
+    if (s + 1 < nsteps) {
+      if (sdma) wait_vmcnt_le<6>(); else wait_vmcnt_le<5>();
+    } else {
+      wait_vmcnt_le<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    if (s + 2 < nsteps) issue(next2, s + 2);
+    compute(cur);
+  };
+
+  issue(lds0, 0);
+  if (nsteps > 1) issue(lds1, 1);
+  for (int s = 0; s < nsteps; s += 3) {
+    step(lds0, lds2, s);
+    if (s + 1 < nsteps) step(lds1, lds0, s + 1);
+    if (s + 2 < nsteps) step(lds2, lds1, s + 2);
+  }
+
+  const float gw = *w_g;
+#pragma unroll
+  for (int bt = 0; bt < 4; ++bt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + wm * 128 + bt * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+      if (row >= B) continue;
+      const float rsc = rowscale[row] * gw;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int col = n0 + wn * 64 + nt * 32 + l32;
+        if (col < N) y[(int64_t)row * N + col] = (_Float16)(acc[bt][nt][r] * rsc);
+      }
+    }
+  }
+}
+
 bool use_skinny(int64_t B, int64_t K) { return B <= 16 && skinny_lds_bytes(B, K) <= kSkinnyDynMax; }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -399,6 +737,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
     if (attr_err == hipSuccess)
       attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTiledLds);
+
   });
   if (attr_err != hipSuccess) return attr_err;
   const int B = (int)g.B, N = (int)g.N, K = (int)g.K;
@@ -415,8 +754,13 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   hipLaunchKernelGGL(a_to_f16_rows, dim3((unsigned)B), dim3(256), 0, s, g.a, g.a_scale, a16,
                      rowscale, K);
   const int tiles_m = (B + kTM - 1) / kTM, tiles_n = (N + kTN - 1) / kTN;
-  hipLaunchKernelGGL(gemm_tiled, dim3((unsigned)(tiles_m * tiles_n)), dim3(kTThreads), kTiledLds,
-                     s, a16, rowscale, g.w, g.w_sf, g.w_g, y, B, N, K, tiles_n);
+  if (K % kTK == 0) {
+    hipLaunchKernelGGL(gemm_tiled_pipe8, dim3((unsigned)(tiles_m * tiles_n)), dim3(kP2Threads),
+                       kPipeLds, s, a16, rowscale, g.w, g.w_sf, g.w_g, y, B, N, K, tiles_m, tiles_n);
+  } else {
+    hipLaunchKernelGGL(gemm_tiled, dim3((unsigned)(tiles_m * tiles_n)), dim3(kTThreads), kTiledLds,
+                       s, a16, rowscale, g.w, g.w_sf, g.w_g, y, B, N, K, tiles_n);
+  }
   return hipGetLastError();
 }
 
