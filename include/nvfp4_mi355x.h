@@ -121,7 +121,8 @@ int32_t nvfp4_act_quant(const void* x, int32_t dtype, int64_t rows, int64_t k_ou
  *   y        : [B, N] fp16 out (round-to-nearest-even from fp32 accumulation)
  *   workspace: nvfp4_gemm_workspace_size() bytes (may be 0 -> NULL allowed)
  * Requires B >= 0, N > 0, K > 0, K % 32 == 0 (whole bytes of 16-blocks in
- * pairs).  B == 0 is a no-op.
+ * pairs); w 16-byte aligned, w_sf 2-byte aligned, a_scale and w_gscale
+ * 4-byte aligned (EINVAL otherwise).  B == 0 is a no-op.
  */
 int32_t nvfp4_gemm(const uint8_t* a, const float* a_scale, const uint8_t* w, const uint8_t* w_sf,
                    const float* w_gscale, void* y, int64_t B, int64_t N, int64_t K,
@@ -149,7 +150,8 @@ size_t nvfp4_gemm_workspace_size(int64_t B, int64_t N, int64_t K);
  * by their sum when norm_topk_prob, times routed_scaling.
  * Requires experts % n_group == 0, 1 <= topk_group <= n_group,
  * 1 <= top_k <= topk_group * experts / n_group, top_k <= 16, experts <= 256,
- * hidden % 32 == 0, inter % 32 == 0.
+ * hidden % 32 == 0, inter % 32 == 0, tokens <= 16384; x, w1, w2 16-byte
+ * aligned, out 8-byte aligned, block scales 2-byte aligned (EINVAL otherwise).
  */
 int32_t nvfp4_moe_w4a16(const float* router_logits, const float* correction_bias, const void* x,
                         const uint8_t* w1, const uint8_t* w1_sf, const float* w1_g,

@@ -147,6 +147,10 @@ int32_t nvfp4_moe_w4a16(const float* router_logits, const float* correction_bias
   if (!router_logits || !correction_bias || !x || !w1 || !w1_sf || !w1_g || !w2 || !w2_sf ||
       !w2_g || !out)
     return NVFP4_EINVAL;
+  if (((uintptr_t)x % 16) != 0 || ((uintptr_t)out % 8) != 0 || ((uintptr_t)w1 % 16) != 0 ||
+      ((uintptr_t)w2 % 16) != 0 || ((uintptr_t)w1_sf % 2) != 0 || ((uintptr_t)w2_sf % 2) != 0 ||
+      !aligned4(router_logits) || !aligned4(correction_bias) || !aligned4(w1_g) || !aligned4(w2_g))
+    return NVFP4_EINVAL;
   const size_t need = nvfp4::moe_workspace_bytes(tokens, experts, top_k, hidden, inter);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % 256) != 0)
     return NVFP4_EWORKSPACE;

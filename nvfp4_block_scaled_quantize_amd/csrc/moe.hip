@@ -26,6 +26,8 @@
 #include "device_common.h"
 #include "internal.h"
 
+#include <mutex>
+
 namespace nvfp4 {
 
 namespace {
@@ -197,6 +199,76 @@ __device__ int gather_pairs(const int32_t* __restrict__ ids, int P, int e, int* 
   return cnt_sh;
 }
 
+// Pairs routed to expert e, in pair order: plist[i] = pair index, tlist[i] =
+// its token (pair / top_k).  Every wave scans a contiguous share of the
+// routing table (its ids are loaded in one round), a prefix over the waves
+// orders the shares, a second ballot pass writes the lists.
+constexpr int kGatherRegs = 8;   // routing-table chunks of 64 held per wave per round
+
+__device__ int gather_pairs_all(const int32_t* __restrict__ ids, int P, int top_k, int e,
+                                int* plist, int* tlist) {
+  __shared__ int wcnt[16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int nchunks = (P + 63) / 64;
+  const int per = (nchunks + nw - 1) / nw;
+  const int c0 = wave * per, c1 = (c0 + per < nchunks) ? c0 + per : nchunks;
+  uint64_t masks[kGatherRegs];
+  int cnt = 0;
+  const bool inreg = (c1 - c0) <= kGatherRegs;
+  if (inreg) {
+    int v[kGatherRegs];
+#pragma unroll
+    for (int i = 0; i < kGatherRegs; ++i) {
+      const int p = (c0 + i) * 64 + lane;
+      v[i] = (c0 + i < c1 && p < P) ? ids[p] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kGatherRegs; ++i) {
+      masks[i] = __ballot(v[i] == e);
+      cnt += __popcll(masks[i]);
+    }
+  } else {
+    for (int c = c0; c < c1; ++c) {
+      const int p = c * 64 + lane;
+      cnt += __popcll(__ballot((p < P) && ids[p] == e));
+    }
+  }
+  if (lane == 0) wcnt[wave] = cnt;
+  __syncthreads();
+  int base = 0, total = 0;
+  for (int i = 0; i < nw; ++i) {
+    if (i < wave) base += wcnt[i];
+    total += wcnt[i];
+  }
+  const uint64_t lt = (1ull << lane) - 1ull;
+  if (inreg) {
+#pragma unroll
+    for (int i = 0; i < kGatherRegs; ++i) {
+      const int p = (c0 + i) * 64 + lane;
+      if ((masks[i] >> lane) & 1ull) {
+        const int slot = base + __popcll(masks[i] & lt);
+        plist[slot] = p;
+        tlist[slot] = p / top_k;
+      }
+      base += __popcll(masks[i]);
+    }
+  } else {
+    for (int c = c0; c < c1; ++c) {
+      const int p = c * 64 + lane;
+      const bool hit = (p < P) && ids[p] == e;
+      const uint64_t m = __ballot(hit);
+      if (hit) {
+        const int slot = base + __popcll(m & lt);
+        plist[slot] = p;
+        tlist[slot] = p / top_k;
+      }
+      base += __popcll(m);
+    }
+  }
+  __syncthreads();
+  return total;
+}
+
 __device__ __forceinline__ v8h dequant8_w(uint32_t codes, _Float16 s16) {
   const v2h s2 = {s16, s16};
   const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s2;
@@ -329,6 +401,217 @@ moe_fc(const void* __restrict__ act, const int32_t* __restrict__ ids, int P, int
   }
 }
 
+// Streaming version of fc1/fc2 (the one launched).  One workgroup = 4 waves
+// = 64 weight rows of one expert, each wave 16 rows over the whole K (two
+// workgroups fit a CU, so one computes while the other waits on memory).
+// Each lane issues all of its weight-code loads (32 codes + 2 E4M3 bytes per
+// 128-k chunk, up to 2048 k) before any arithmetic.  The expert's token rows
+// are staged in LDS as FP16 in 256-k chunks (fc2 applies the per-pair power
+// of two while staging), double-buffered, and feed v_mfma_f32_16x16x32_f16 as
+// the second operand, 64 tokens per pass.
+constexpr int kMsThreads = 256;
+constexpr int kMsRows = 64;
+constexpr int kMsKC = 256;               // staged k per LDS chunk
+constexpr int kMsTok = 64;               // tokens per pass (4 tiles of 16)
+constexpr int kMsSB = 2048;              // k per register superblock (16 chunks of 128)
+constexpr int kMsPitch = kMsKC + 8;      // halves per staged token row (+16 B skew)
+
+size_t moe_stream_lds(int tokens) {
+  return 2 * align256((size_t)tokens * 4) + 2 * (size_t)kMsTok * kMsPitch * 2;
+}
+
+template <int FC>
+__global__ void __launch_bounds__(kMsThreads)
+moe_fc_stream(const void* __restrict__ act, const int32_t* __restrict__ ids, int P, int top_k,
+              uint32_t* __restrict__ pmax, const uint8_t* __restrict__ w,
+              const uint8_t* __restrict__ w_sf, const float* __restrict__ w_g, int N, int K,
+              float* __restrict__ out, int tok_off) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
+  int* plist = reinterpret_cast<int*>(sm);
+  int* tlist = reinterpret_cast<int*>(sm + tok_off / 2);
+  _Float16* xsb[2] = {reinterpret_cast<_Float16*>(sm + tok_off),
+                      reinterpret_cast<_Float16*>(sm + tok_off + kMsTok * kMsPitch * 2)};
+  const int e = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int nbase = blockIdx.x * kMsRows + wave * 16;
+  const int nrow = nbase + r16;
+  const bool nvalid = nrow < N;
+  const int64_t kb2 = K / 2, kb16 = K / 16;
+  const uint8_t* wr = w + ((int64_t)e * N + (nvalid ? nrow : 0)) * kb2;
+  const uint8_t* sr = w_sf + ((int64_t)e * N + (nvalid ? nrow : 0)) * kb16;
+  const v8h zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+  constexpr int kStageVec = (kMsTok * kMsKC / 8) / kMsThreads;   // 8-element vectors per thread
+
+  const int cnt = gather_pairs_all(ids, P, top_k, e, plist, tlist);
+  if (cnt == 0) return;
+  const float ge = w_g[e];
+
+  uint4 wc[16];
+  uint32_t ws[16];
+  auto load_w = [&](int kb) {
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const int k = kb + 128 * c + 32 * g;
+      const bool v = nvalid && k < K;
+      wc[c] = v ? *reinterpret_cast<const uint4*>(wr + k / 2) : make_uint4(0, 0, 0, 0);
+      ws[c] = v ? (uint32_t)*reinterpret_cast<const uint16_t*>(sr + k / 16) : 0u;
+    }
+  };
+
+  // staging of token rows: global -> registers -> LDS (FP16)
+  v8h stg[kStageVec];
+  auto stage_load = [&](int t0, int kc) {
+#pragma unroll
+    for (int i = 0; i < kStageVec; ++i) {
+      const int v = tid + kMsThreads * i;
+      const int slot = v / (kMsKC / 8), kq = v % (kMsKC / 8);
+      const int k = kc + 8 * kq;
+      v8h val = zero8;
+      if (t0 + slot < cnt && k < K) {
+        if constexpr (FC == 1) {
+          val = *reinterpret_cast<const v8h*>(reinterpret_cast<const _Float16*>(act) +
+                                              (int64_t)tlist[t0 + slot] * K + k);
+        } else {
+          const int p = plist[t0 + slot];
+          const uint32_t mb = pmax[p];
+          const int ex = (mb == 0u) ? 0 : (int)((mb >> 23) & 0xFFu) - 127;
+          const float sc = __builtin_ldexpf(1.0f, -ex);
+          const float* src = reinterpret_cast<const float*>(act) + (int64_t)p * K + k;
+          const float4 lo = *reinterpret_cast<const float4*>(src);
+          const float4 hi = *reinterpret_cast<const float4*>(src + 4);
+          val[0] = (_Float16)(lo.x * sc); val[1] = (_Float16)(lo.y * sc);
+          val[2] = (_Float16)(lo.z * sc); val[3] = (_Float16)(lo.w * sc);
+          val[4] = (_Float16)(hi.x * sc); val[5] = (_Float16)(hi.y * sc);
+          val[6] = (_Float16)(hi.z * sc); val[7] = (_Float16)(hi.w * sc);
+        }
+      }
+      stg[i] = val;
+    }
+  };
+  auto stage_store = [&](_Float16* xs) {
+#pragma unroll
+    for (int i = 0; i < kStageVec; ++i) {
+      const int v = tid + kMsThreads * i;
+      const int slot = v / (kMsKC / 8), kq = v % (kMsKC / 8);
+      *reinterpret_cast<v8h*>(xs + slot * kMsPitch + 8 * kq) = stg[i];
+    }
+  };
+
+  // one superblock of up to 2048 k for tokens [t0, t0+64)
+  auto superblock = [&](int t0, int kb, v4f* acc) {
+    stage_store(xsb[0]);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kMsSB / kMsKC; ++q) {
+      const int kc = kb + q * kMsKC;
+      if (kc >= K) break;
+      const bool more = (q + 1 < kMsSB / kMsKC) && (kc + kMsKC < K);
+      if (more) stage_load(t0, kc + kMsKC);        // next chunk's loads in flight
+      const _Float16* xs = xsb[q & 1];
+#pragma unroll
+      for (int c2 = 0; c2 < kMsKC / 128; ++c2) {
+        const int c = q * (kMsKC / 128) + c2;     // chunk within the superblock
+        const int k = kc + 128 * c2 + 32 * g;
+        if (kc + 128 * c2 >= K) break;
+        const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)ws[c], 0);
+        const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)ws[c], 1);
+        v8h af[4];
+        af[0] = dequant8_w(wc[c].x, s0);
+        af[1] = dequant8_w(wc[c].y, s0);
+        af[2] = dequant8_w(wc[c].z, s1);
+        af[3] = dequant8_w(wc[c].w, s1);
+        const bool kv = k < K;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          if (t0 + 16 * tt >= cnt) break;
+          const _Float16* xrow = xs + (16 * tt + r16) * kMsPitch + 128 * c2 + 32 * g;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const v8h bf = kv ? *reinterpret_cast<const v8h*>(xrow + 8 * m) : zero8;
+            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[m], bf, acc[tt], 0, 0, 0);
+          }
+        }
+      }
+      if (more) stage_store(xsb[(q + 1) & 1]);
+      __syncthreads();
+    }
+  };
+
+  auto epilogue = [&](int t0, const v4f* acc) {
+    // D[i][j] -> weight row nbase + 4g + r, token slot t0 + 16tt + (lane & 15)
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      if (t0 + 16 * tt >= cnt) break;
+      const int slot = t0 + 16 * tt + r16;
+      const bool sv = slot < cnt;
+      const int p = sv ? plist[slot] : 0;
+      float scale = ge;
+      if constexpr (FC == 2) {
+        const uint32_t mb = pmax[p];
+        const int ex = (mb == 0u) ? 0 : (int)((mb >> 23) & 0xFFu) - 127;
+        scale = __builtin_ldexpf(ge, ex);
+      }
+      float vmax = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int n = nbase + 4 * g + r;
+        float v = acc[tt][r] * scale;
+        if constexpr (FC == 1) {
+          v = relu2_f32(v);
+          vmax = __builtin_fmaxf(vmax, v);
+        }
+        if (sv && n < N) out[(int64_t)p * N + n] = v;
+      }
+      if constexpr (FC == 1) {
+        vmax = __builtin_fmaxf(vmax, __shfl_xor(vmax, 16, 64));
+        vmax = __builtin_fmaxf(vmax, __shfl_xor(vmax, 32, 64));
+        if (sv && g == 0) atomicMax(pmax + p, __float_as_uint(vmax));
+      }
+    }
+  };
+
+  if (cnt <= kMsTok && K <= kMsSB) {
+    // common case: one pass, one superblock, straight-line
+    load_w(0);
+    stage_load(0, 0);
+    v4f acc[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) acc[tt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    superblock(0, 0, acc);
+    epilogue(0, acc);
+    return;
+  }
+  for (int t0 = 0; t0 < cnt; t0 += kMsTok) {
+    v4f acc[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) acc[tt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int kb = 0; kb < K; kb += kMsSB) {
+      load_w(kb);
+      stage_load(t0, kb);
+      superblock(t0, kb, acc);
+    }
+    epilogue(t0, acc);
+  }
+}
+
+// out[t] = sum_j w[t,j] * o[t*top_k + j], four outputs per thread.
+__global__ void __launch_bounds__(256)
+moe_combine4(const float* __restrict__ o, const float* __restrict__ wts, int top_k, int H,
+             _Float16* __restrict__ out) {
+  const int64_t t = blockIdx.x;
+  const int n = (blockIdx.y * 256 + threadIdx.x) * 4;
+  if (n >= H) return;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < top_k; ++j) {
+    const float wj = wts[t * top_k + j];
+    const float4 v = *reinterpret_cast<const float4*>(o + (t * top_k + j) * H + n);
+    s.x += wj * v.x; s.y += wj * v.y; s.z += wj * v.z; s.w += wj * v.w;
+  }
+  v4h r = {(_Float16)s.x, (_Float16)s.y, (_Float16)s.z, (_Float16)s.w};
+  *reinterpret_cast<v4h*>(out + t * H + n) = r;
+}
+
 __global__ void __launch_bounds__(256)
 moe_combine(const float* __restrict__ o, const float* __restrict__ wts, int top_k, int H,
             _Float16* __restrict__ out) {
@@ -351,19 +634,30 @@ size_t moe_workspace_bytes(int tokens, int experts, int top_k, int hidden, int i
 hipError_t launch_moe(const MoeArgs& m, hipStream_t s) {
   const int P = m.tokens * m.top_k;
   if (m.tokens > 16384) return hipErrorNotSupported;   // the per-expert pair list lives in LDS
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, []() {
+    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_fc_stream<1>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 1024);
+    if (attr_err == hipSuccess)
+      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_fc_stream<2>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 1024);
+  });
+  if (attr_err != hipSuccess) return attr_err;
   MoeWs ws = carve(m.workspace, P, m.hidden, m.inter);
   hipLaunchKernelGGL(moe_route, dim3((m.tokens + 3) / 4), dim3(256), 0, s, m.logits, m.bias,
                      m.tokens, m.experts, m.top_k, m.n_group, m.topk_group, m.norm, m.scaling,
                      ws.ids, ws.wts, ws.pmax, m.ids_out, m.w_out);
-  const size_t lds = (size_t)m.tokens * sizeof(int);
-  hipLaunchKernelGGL(moe_fc<1>, dim3((m.inter + kFcRows - 1) / kFcRows, m.experts), dim3(kFcThreads),
-                     lds, s, m.x, ws.ids, P, m.top_k, ws.pmax, m.w1, m.w1_sf, m.w1_g, m.inter,
-                     m.hidden, ws.h);
-  hipLaunchKernelGGL(moe_fc<2>, dim3((m.hidden + kFcRows - 1) / kFcRows, m.experts), dim3(kFcThreads),
-                     lds, s, ws.h, ws.ids, P, m.top_k, ws.pmax, m.w2, m.w2_sf, m.w2_g, m.hidden,
-                     m.inter, ws.o);
-  hipLaunchKernelGGL(moe_combine, dim3(m.tokens), dim3(256), 0, s, ws.o, ws.wts, m.top_k, m.hidden,
-                     reinterpret_cast<_Float16*>(m.out));
+  const size_t lds = moe_stream_lds(m.tokens);
+  const int tok_off = 2 * (int)align256((size_t)m.tokens * 4);
+  hipLaunchKernelGGL(moe_fc_stream<1>, dim3((m.inter + kMsRows - 1) / kMsRows, m.experts),
+                     dim3(kMsThreads), lds, s, m.x, ws.ids, P, m.top_k, ws.pmax, m.w1, m.w1_sf,
+                     m.w1_g, m.inter, m.hidden, ws.h, tok_off);
+  hipLaunchKernelGGL(moe_fc_stream<2>, dim3((m.hidden + kMsRows - 1) / kMsRows, m.experts),
+                     dim3(kMsThreads), lds, s, ws.h, ws.ids, P, m.top_k, ws.pmax, m.w2, m.w2_sf,
+                     m.w2_g, m.hidden, m.inter, ws.o, tok_off);
+  hipLaunchKernelGGL(moe_combine4, dim3(m.tokens, (m.hidden + 1023) / 1024), dim3(256), 0, s, ws.o,
+                     ws.wts, m.top_k, m.hidden, reinterpret_cast<_Float16*>(m.out));
   return hipGetLastError();
 }
 
