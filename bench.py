@@ -13,7 +13,9 @@ quantize + GEMM small case, MoE) are measured after it and reported under
 Timing: inputs are resident in HBM before the timed region; W warmup steps,
 then exactly K steps between synchronizations, timed with HIP events on the
 stream the kernels run on; per-call events give the average duration of the
-GEMM call and of the quantize call.
+GEMM call and of the quantize call.  The micro-second workloads (decode,
+small, MoE, SwiGLU) are timed by replaying a HIP graph of many calls, so the
+host's per-call launch cost is not counted as GPU time.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
 """
@@ -45,6 +47,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--quick", action="store_true", help="skip the secondary workloads and the CPU baseline")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--only", choices=["prefill", "decode", "swiglu", "small", "moe", "copy"],
+                   help="run one workload and print its measurement (for profiler runs)")
     return p.parse_args()
 
 
@@ -118,9 +122,35 @@ def run_prefill(torch, nv, si, steps, warmup):
                 flops=2.0 * B * N * K, qbytes=quant_bytes(B, K, K), gbytes=gemm_bytes(B, N, K))
 
 
-def run_decode(torch, nv, si, B, iters=50):
-    """Decode GEMM (one rank's K-share) with the weights rotated through > 512 MB
-    so the 256 MB Infinity Cache cannot hold them."""
+def graph_time_ms(torch, fns, reps=5):
+    """Average GPU time per call of `fns` (a list of launch callables), timed by
+    replaying a HIP graph that holds one call of each: the host-side cost of
+    issuing micro-second kernels one by one does not enter the figure."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * len(fns))
+
+
+def run_decode(torch, nv, si, B, iters=None):
+    """Decode GEMM (one rank's K-share) with the weights rotated through 32
+    copies (> 512 MB) so the 256 MB Infinity Cache cannot hold them."""
     c = si.CONFIGS["C2"]
     K, N = c["K"], c["N"]
     dev = torch.device("cuda:0")
@@ -131,42 +161,26 @@ def run_decode(torch, nv, si, B, iters=50):
     x = a.to(dev)
     qa = nv.act_quant(x, "none")
     y = torch.empty((B, N), dtype=torch.float16, device=dev)
-    stream = torch.cuda.current_stream()
-    for i in range(copies):
-        nv.gemm(qa["codes"], qa["scale"], *Ws[i], out=y)
-    torch.cuda.synchronize()
-    tg, tq = EventTimer(torch, stream), EventTimer(torch, stream)
-    for i in range(iters):
-        tq(lambda: nv.act_quant(x, "none", out=qa))
-        Wi = Ws[i % copies]
-        tg(lambda: nv.gemm(qa["codes"], qa["scale"], *Wi, out=y))
-    torch.cuda.synchronize()
+    ms_gemm = graph_time_ms(torch, [(lambda Wi=Wi: nv.gemm(qa["codes"], qa["scale"], *Wi, out=y)) for Wi in Ws])
+    ms_quant = graph_time_ms(torch, [lambda: nv.act_quant(x, "none", out=qa)] * 8)
     gb = gemm_bytes(B, N, K)
-    return dict(B=B, us_gemm=tg.mean_ms() * 1e3, us_quant=tq.mean_ms() * 1e3, gemm_bytes=gb,
-                gemm_GBps=gb / (tg.mean_ms() * 1e-3) / 1e9,
-                hbm_frac=gb / (tg.mean_ms() * 1e-3) / 1e9 / HBM_PEAK_GBS)
+    return dict(B=B, us_gemm=ms_gemm * 1e3, us_quant=ms_quant * 1e3, gemm_bytes=gb,
+                gemm_GBps=gb / (ms_gemm * 1e-3) / 1e9, hbm_frac=gb / (ms_gemm * 1e-3) / 1e9 / HBM_PEAK_GBS)
 
 
-def run_swiglu(torch, nv, si, iters=20):
+def run_swiglu(torch, nv, si, iters=10):
     c = si.CONFIGS["C4"]
     rows, H = c["rows"], c["H"]
     dev = torch.device("cuda:0")
     x = si.swiglu_input().to(dev)
     out = nv.act_quant(x, "swiglu", want_scale=False)
-    stream = torch.cuda.current_stream()
-    for _ in range(3):
-        nv.act_quant(x, "swiglu", out=out)
-    torch.cuda.synchronize()
-    t = EventTimer(torch, stream)
-    for _ in range(iters):
-        t(lambda: nv.act_quant(x, "swiglu", out=out))
-    torch.cuda.synchronize()
+    ms = graph_time_ms(torch, [lambda: nv.act_quant(x, "swiglu", out=out)] * iters, reps=2)
     by = quant_bytes(rows, 2 * H, H, scale=False)
-    return dict(rows=rows, H=H, us=t.mean_ms() * 1e3, bytes=by, GBps=by / (t.mean_ms() * 1e-3) / 1e9,
-                hbm_frac=by / (t.mean_ms() * 1e-3) / 1e9 / HBM_PEAK_GBS)
+    return dict(rows=rows, H=H, us=ms * 1e3, bytes=by, GBps=by / (ms * 1e-3) / 1e9,
+                hbm_frac=by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
 
 
-def run_small(torch, nv, si, iters=50):
+def run_small(torch, nv, si, iters=20):
     c = si.CONFIGS["C1"]
     B, K, N = c["B"], c["K"], c["N"]
     dev = torch.device("cuda:0")
@@ -175,19 +189,15 @@ def run_small(torch, nv, si, iters=50):
     wq = nv.quantize(w.to(dev), group_rows=N, want_scale=False)
     qa = nv.act_quant(x, "none")
     y = nv.gemm(qa["codes"], qa["scale"], wq["codes"], wq["sf"], wq["g_dec"])
-    stream = torch.cuda.current_stream()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(iters):
+
+    def step():
         nv.act_quant(x, "none", out=qa)
         nv.gemm(qa["codes"], qa["scale"], wq["codes"], wq["sf"], wq["g_dec"], out=y)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return dict(B=B, K=K, N=N, us_step=e0.elapsed_time(e1) / iters * 1e3)
+    ms = graph_time_ms(torch, [step] * iters)
+    return dict(B=B, K=K, N=N, us_step=ms * 1e3)
 
 
-def run_moe(torch, nv, si, iters=20):
+def run_moe(torch, nv, si, iters=None):
     c = si.CONFIGS["C5"]
     dev = torch.device("cuda:0")
     d = si.moe_inputs()
@@ -197,25 +207,28 @@ def run_moe(torch, nv, si, iters=20):
     args = [torch.from_numpy(d["logits"]).to(dev), torch.from_numpy(d["bias"]).to(dev), d["x"].to(dev),
             w1["codes"].view(E, I, Hd // 2), w1["sf"].view(E, I, Hd // 16), w1["g_dec"],
             w2["codes"].view(E, Hd, I // 2), w2["sf"].view(E, Hd, I // 16), w2["g_dec"]]
-    copies = 4
+    copies = 4   # 4 x 151 MB of expert weights rotate past the 256 MB Infinity Cache
     sets = [args] + [[t.clone() if i >= 3 else t for i, t in enumerate(args)] for _ in range(copies - 1)]
     out = torch.empty((T, Hd), dtype=torch.float16, device=dev)
     ws = torch.empty(nv.moe_workspace_size(T, E, c["top_k"], Hd, I), dtype=torch.uint8, device=dev)
     kw = dict(top_k=c["top_k"], n_group=c["n_group"], topk_group=c["topk_group"],
               norm_topk_prob=c["norm_topk_prob"], routed_scaling=c["routed_scaling"], out=out, workspace=ws)
-    for s in sets:
-        nv.moe_w4a16(*s, **kw)
-    torch.cuda.synchronize()
-    t = EventTimer(torch, torch.cuda.current_stream())
-    for i in range(iters):
-        s = sets[i % copies]
-        t(lambda: nv.moe_w4a16(*s, **kw))
-    torch.cuda.synchronize()
+    ms = graph_time_ms(torch, [(lambda st=st: nv.moe_w4a16(*st, **kw)) for st in sets], reps=3)
     wbytes = E * (I * Hd // 2 + I * Hd // 16 + Hd * I // 2 + Hd * I // 16) + 2 * E * 4
     by = wbytes + T * Hd * 2 * 2 + T * E * 4 + E * 4
-    return dict(T=T, E=E, us=t.mean_ms() * 1e3, bytes=by, GBps=by / (t.mean_ms() * 1e-3) / 1e9,
-                hbm_frac=by / (t.mean_ms() * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                flops=2.0 * T * c["top_k"] * (2 * Hd * I))
+    return dict(T=T, E=E, us=ms * 1e3, bytes=by, GBps=by / (ms * 1e-3) / 1e9,
+                hbm_frac=by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, flops=2.0 * T * c["top_k"] * (2 * Hd * I))
+
+
+def run_copy(torch):
+    """A plain 256 MiB device copy, three times: the reference for scaling the
+    FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    x = torch.empty(256 * 1024 * 1024, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    return {"bytes_read_per_copy": x.numel(), "bytes_written_per_copy": y.numel()}
 
 
 def cpu_baseline(si, pre):
@@ -225,7 +238,7 @@ def cpu_baseline(si, pre):
     import numpy as np
     import oracle
     from threadpoolctl import threadpool_info
-    R = 16
+    R = 4096
     c = si.CONFIGS["C3"]
     K, N = c["K"], c["N"]
     a, w = si.gemm_inputs("C3")
@@ -242,11 +255,18 @@ def cpu_baseline(si, pre):
                       "reference against the full %dx%d weight (%.1f s)" % (R, c["B"], N, K, dt)}
 
 
-def load_traffic(name):
+def load_traffic():
+    """HBM bytes per GEMM call from the committed counter run, or None when the
+    GEMM source has changed since the counters were taken."""
+    import hashlib
     try:
         with open(ALGO_TRAFFIC_FILE) as f:
-            return json.load(f).get(name)
-    except (OSError, ValueError):
+            t = json.load(f)
+        src = os.path.join(ROOT, "nvfp4_block_scaled_quantize_amd", "csrc", "gemm.hip")
+        with open(src, "rb") as f:
+            h = hashlib.sha256(f.read()).hexdigest()
+        return t["gemm_call_bytes"] if t.get("gemm_source_sha256") == h else None
+    except (OSError, ValueError, KeyError):
         return None
 
 
@@ -262,6 +282,15 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.only:
+        fn = {"prefill": lambda: run_prefill(torch, nv, si, 3, 1),
+              "decode": lambda: {B: run_decode(torch, nv, si, B) for B in (1, 4, 8)},
+              "swiglu": lambda: run_swiglu(torch, nv, si, iters=3),
+              "small": lambda: run_small(torch, nv, si),
+              "moe": lambda: run_moe(torch, nv, si),
+              "copy": lambda: run_copy(torch)}[args.only]
+        print(json.dumps({"only": args.only, "result": fn()}, default=str), flush=True)
+        return
     log("prefill: act_quant [4096,8192] + gemm 4096x8192x8192, %d warmup + %d steps" % (args.warmup, args.steps))
     pre = run_prefill(torch, nv, si, args.steps, args.warmup)
     value = pre["flops"] / (pre["ms_step"] * 1e-3) / 1e12
@@ -307,7 +336,7 @@ def main():
         "roofline": {"kernel": "nvfp4_gemm (prefill)", "bound": "mfma", "achieved": round(gemm_tflops, 1),
                      "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / FP16_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": load_traffic("gemm_tiled")},
+                     "traffic": load_traffic(), "traffic_unit": "bytes per call"},
         "cpu_baseline": cpu,
         "workloads": workloads,
     }
