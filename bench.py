@@ -47,7 +47,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--quick", action="store_true", help="skip the secondary workloads and the CPU baseline")
     p.add_argument("--no-cpu", action="store_true")
-    p.add_argument("--only", choices=["prefill", "decode", "swiglu", "small", "moe", "copy"],
+    p.add_argument("--only", choices=["prefill", "decode", "swiglu", "quant", "small", "moe", "copy"],
                    help="run one workload and print its measurement (for profiler runs)")
     return p.parse_args()
 
@@ -168,6 +168,24 @@ def run_decode(torch, nv, si, B, iters=None):
                 gemm_GBps=gb / (ms_gemm * 1e-3) / 1e9, hbm_frac=gb / (ms_gemm * 1e-3) / 1e9 / HBM_PEAK_GBS)
 
 
+def run_quant_rotating(torch, nv, si, copies=5, reps=4):
+    """Per-token quantize of the prefill activations ([4096, 8192] bf16, codes +
+    E4M3 bytes + globals + combined scales) with the input rotated through
+    `copies` buffers (5 x 64 MB > the 256 MB Infinity Cache), so every call
+    reads its input from HBM."""
+    c = si.CONFIGS["C3"]
+    B, K = c["B"], c["K"]
+    dev = torch.device("cuda:0")
+    a, _ = si.gemm_inputs("C3", N=16)
+    xs = [a.to(dev) for _ in range(copies)]
+    outs = [nv.act_quant(x, "none") for x in xs]
+    ms = graph_time_ms(torch, [(lambda x=x, o=o: nv.act_quant(x, "none", out=o)) for x, o in zip(xs, outs)],
+                       reps=reps)
+    by = quant_bytes(B, K, K)
+    return dict(rows=B, K=K, us=ms * 1e3, bytes=by, GBps=by / (ms * 1e-3) / 1e9,
+                hbm_frac=by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+
+
 def run_swiglu(torch, nv, si, iters=10):
     c = si.CONFIGS["C4"]
     rows, H = c["rows"], c["H"]
@@ -286,6 +304,7 @@ def main():
         fn = {"prefill": lambda: run_prefill(torch, nv, si, 3, 1),
               "decode": lambda: {B: run_decode(torch, nv, si, B) for B in (1, 4, 8)},
               "swiglu": lambda: run_swiglu(torch, nv, si, iters=3),
+              "quant": lambda: run_quant_rotating(torch, nv, si),
               "small": lambda: run_small(torch, nv, si),
               "moe": lambda: run_moe(torch, nv, si),
               "copy": lambda: run_copy(torch)}[args.only]
@@ -309,6 +328,9 @@ def main():
             log("decode B=%d" % B)
             workloads["decode_C2_B%d" % B] = {k: (round(v, 4) if isinstance(v, float) else v)
                                               for k, v in run_decode(torch, nv, si, B).items()}
+        log("activation quantize, rotating inputs")
+        workloads["quant_C3_rotating"] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                          for k, v in run_quant_rotating(torch, nv, si).items()}
         log("swiglu quantize")
         workloads["swiglu_quant_C4"] = {k: (round(v, 4) if isinstance(v, float) else v)
                                         for k, v in run_swiglu(torch, nv, si).items()}

@@ -11,25 +11,31 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 
-// 1 if the current device is gfx950, 0 if not, -1 if HIP reports an error.
-// Device properties are queried once per device.
-int current_device_ok() {
+struct DeviceInfo {
+  int ok;        // 1 if gfx950, 0 if not
+  int num_cus;   // compute units
+};
+
+// Properties of the current device, queried once per device; nullptr if HIP
+// reports an error.
+const DeviceInfo* current_device() {
   static std::once_flag once[kMaxDevices];
-  static int ok[kMaxDevices];
+  static DeviceInfo info[kMaxDevices];
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
   std::call_once(once[dev], [dev]() {
     hipDeviceProp_t p;
-    ok[dev] = (hipGetDeviceProperties(&p, dev) == hipSuccess &&
-               strncmp(p.gcnArchName, "gfx950", 6) == 0) ? 1 : 0;
+    const bool got = hipGetDeviceProperties(&p, dev) == hipSuccess;
+    info[dev].ok = (got && strncmp(p.gcnArchName, "gfx950", 6) == 0) ? 1 : 0;
+    info[dev].num_cus = got ? p.multiProcessorCount : 0;
   });
-  return ok[dev];
+  return &info[dev];
 }
 
 int32_t device_status() {
-  const int d = current_device_ok();
-  if (d < 0) return NVFP4_EHIP;
-  return d ? NVFP4_OK : NVFP4_EUNSUPPORTED;
+  const DeviceInfo* d = current_device();
+  if (!d) return NVFP4_EHIP;
+  return d->ok ? NVFP4_OK : NVFP4_EUNSUPPORTED;
 }
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP; }
@@ -85,6 +91,7 @@ static int32_t quantize_common(const void* x, int32_t dtype, int64_t rows, int64
   }
   const int32_t ds = device_status();
   if (ds != NVFP4_OK) return ds;
+  a.num_cus = current_device()->num_cus;
   return hip_status(nvfp4::launch_quantize(a, (hipStream_t)stream));
 }
 

@@ -80,13 +80,15 @@ __device__ __forceinline__ float exp_f32(float x) {
   return __builtin_ldexpf(p, (int)n);
 }
 
-// silu(g) * u with an exactly rounded division.
-__device__ __forceinline__ float swiglu_f32(float g, float u) {
+// silu(g) = g / (1 + exp(-g)) with an exactly rounded division.
+__device__ __forceinline__ float silu_f32(float g) {
   float e = exp_f32(-g);
   float s = 1.0f + e;
-  float q = g / s;
-  return q * u;
+  return g / s;
 }
+
+// SwiGLU output silu(g) * u.
+__device__ __forceinline__ float swiglu_f32(float g, float u) { return silu_f32(g) * u; }
 
 __device__ __forceinline__ float relu2_f32(float x) {
   float r = (x > 0.0f) ? x : 0.0f;
@@ -97,6 +99,23 @@ __device__ __forceinline__ float sigmoid_f32(float l) {
   float e = exp_f32(-l);
   float d = 1.0f + e;
   return 1.0f / d;
+}
+
+// x / 6 correctly rounded.  The product with RN(1/6) is within one ulp of the
+// quotient, and one fma correction step (Markstein) then rounds correctly; this
+// equals the exact quotient for every x in [2^-125, FLT_MAX] (checked for all
+// binary32 values by a host test).  Smaller x (subnormal quotients) and
+// non-finite x divide.
+__device__ __forceinline__ float div6_f32(float x) {
+  const float r = __uint_as_float(0x3E2AAAABu);   // RN(1/6)
+  float q = x * r;
+  const float e = __builtin_fmaf(-q, 6.0f, x);
+  q = __builtin_fmaf(e, r, q);
+  if (!(x >= 0x1p-125f && x <= 3.40282346638528859812e+38f)) {
+    asm volatile("");   // keeps this rare path a branch (not evaluated for every lane)
+    q = x / 6.0f;
+  }
+  return q;
 }
 
 // ---------------------------------------------------------------- scales
@@ -112,7 +131,7 @@ __device__ __forceinline__ void global_scales(float amax, float& g_enc, float& g
 // scale c and its encode factor.
 __device__ __forceinline__ uint32_t block_scale(float amax_b, float g_enc, float g_dec, float& c,
                                                 float& enc) {
-  float sf_f = (amax_b / 6.0f) * g_enc;
+  float sf_f = div6_f32(amax_b) * g_enc;
   float sat = __builtin_fminf(sf_f, 448.0f);
   uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat, 0.0f, 0, false);
   float sfd = __builtin_amdgcn_cvt_f32_fp8((int)pk, 0);
@@ -122,12 +141,25 @@ __device__ __forceinline__ uint32_t block_scale(float amax_b, float g_enc, float
 }
 
 // Eight values -> eight E2M1 codes in one dword (element 0 in bits 3..0).
+// A zero element always gets a zero code with its own sign; this needs care
+// only when enc overflowed to +inf (combined scale below 2^-128), where the
+// product 0 * inf is NaN -- that rare block is encoded directly: non-zero
+// elements saturate to magnitude code 7.
 __device__ __forceinline__ uint32_t pack8_e2m1(const float* v, float enc) {
   uint32_t w = 0;
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0] * enc, v[1] * enc, 1.0f, 0);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2] * enc, v[3] * enc, 1.0f, 1);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4] * enc, v[5] * enc, 1.0f, 2);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6] * enc, v[7] * enc, 1.0f, 3);
+  if (enc == __builtin_inff()) {
+    w = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t b = __float_as_uint(v[i]);
+      const uint32_t code = ((b >> 31) << 3) | ((b << 1) != 0u ? 7u : 0u);
+      w |= code << (4 * i);
+    }
+  }
   return w;
 }
 
@@ -136,6 +168,27 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
   return v;
+}
+
+// Lane exchange inside rows of 16 lanes through DPP (no LDS round trip).
+// CTRL: 0xB1 = quad_perm [1,0,3,2] (lane ^ 1), 0x4E = quad_perm [2,3,0,1]
+// (lane ^ 2), 0x141 = row_half_mirror, 0x140 = row_mirror.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Max over the 64 lanes of a wave, returned as a wave-uniform value.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = __builtin_fmaxf(v, dpp_f32<0xB1>(v));
+  v = __builtin_fmaxf(v, dpp_f32<0x4E>(v));
+  v = __builtin_fmaxf(v, dpp_f32<0x141>(v));
+  v = __builtin_fmaxf(v, dpp_f32<0x140>(v));   // every lane of a 16-lane row holds the row max
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return __builtin_fmaxf(__builtin_fmaxf(r0, r1), __builtin_fmaxf(r2, r3));
 }
 
 }  // namespace nvfp4

@@ -25,6 +25,7 @@ struct QuantArgs {
   float* scale_out;    // may be null
   float* parts;        // workspace: [groups, nparts] partial maxima (group_rows > 1)
   int nparts;
+  int num_cus;         // compute units of the current device (persistent grids)
 };
 
 // Number of partial maxima per group the per-group path uses.

@@ -3,24 +3,34 @@
 // Per-token path (one workgroup per row): the row is read from HBM once and
 // kept in VGPRs between the amax pass and the encode pass -- the role the
 // shared-memory caching of input vectors plays in "perf: optimize per-token
-// nvfp4 quantization kernel" (flashinfer pull request 3237, review).  Each lane
-// owns whole 16-element blocks, so the block amax is an in-lane max and only
-// the row amax needs a wave (DPP/permute) + LDS reduction.  Loads are 16-byte
-// vectors ("Building Custom TensorRT-LLM Plugins for Low-Latency FP8 Inference
-// at Scale", "Fusing the Kernel in CUDA"), consecutive lanes read consecutive
-// 32-byte blocks, and each lane writes its 8 code bytes with one 8-byte store.
+// nvfp4 quantization kernel" (flashinfer pull request 3237, review).  A lane
+// loads units of 8 consecutive values with one 16-byte load, consecutive lanes
+// read consecutive units (each wave load is one contiguous 1 KiB span), so a
+// 16-element block spans an adjacent lane pair and its amax is an in-lane max
+// plus one pair exchange; only the row amax needs a wave + LDS reduction.
+// Each lane writes the 4 code bytes of its unit with one 4-byte store
+// ("Building Custom TensorRT-LLM Plugins for Low-Latency FP8 Inference at
+// Scale", "Fusing the Kernel in CUDA": vector loads, fused encode).
 //
 // The optional activation (SwiGLU: gate = first half of the row, up = second
 // half; ReLU^2) runs in fp32 registers in front of the quantizer, so the
 // activation output never reaches HBM (same article, "The Cost of Non-Fused
 // Quantization").
 //
+// SwiGLU on bf16 inputs with many rows: silu depends only on the 16-bit gate
+// pattern, so each workgroup first tabulates silu in LDS for every bf16 gate
+// with |g| in [2^-24, 256) (8192 entries: both signs, 32 exponents, 128
+// mantissas) using the same binary32 evaluation as the direct path, then
+// streams rows persistently, replacing exp + division by one LDS read.  Gates
+// outside the table (tiny, huge, non-finite) are recomputed directly, so the
+// output is bit-identical to the direct evaluation.
+//
 // Per-group path (per tensor / per expert): a partial-amax kernel writes at
 // most 256 partial maxima per group into the workspace; the row kernel then
 // reduces its group's partials instead of its own row.
 //
 // A scalar fallback handles inputs that are not 16-byte aligned (or codes not
-// 8-byte aligned) and rows longer than the register cache, with identical
+// 4-byte aligned) and rows longer than the register cache, with identical
 // results (same article, "Production Pitfalls & Hard Lessons", item 1).
 #include "device_common.h"
 #include "internal.h"
@@ -29,41 +39,53 @@ namespace nvfp4 {
 
 namespace {
 
-constexpr int kMaxThreads = 256;
+constexpr int kMaxThreads = 256;     // per-row kernel and fallback
+constexpr int kMaxUnits = 16;        // 8-value units per thread held in registers
+constexpr int kTabUnits = 4;         // persistent SwiGLU kernel: units per thread,
+constexpr int kTabThreads = 512;     // at most this many threads per workgroup
+constexpr uint32_t kTabE0 = 103;     // smallest tabulated biased exponent: |g| >= 2^-24
+constexpr int kTabHalf = 32 * 128;   // entries per sign: exponents 103..134 (|g| < 256)
+constexpr int kTabMinRows = 1024;    // below this the per-workgroup table does not pay off
 
-// Loads the 16 activation outputs of block j of a row into y[16].
-template <int DT, int ACT>
-__device__ __forceinline__ void load_block_vec(const uint16_t* __restrict__ xr, int64_t k_out, int j,
-                                               float* y) {
-  if constexpr (ACT == kActSwiglu) {
-    const u32x4* pg = reinterpret_cast<const u32x4*>(xr + 16 * (int64_t)j);
-    const u32x4* pu = reinterpret_cast<const u32x4*>(xr + k_out + 16 * (int64_t)j);
-    const u32x4 g0 = __builtin_nontemporal_load(pg);
-    const u32x4 g1 = __builtin_nontemporal_load(pg + 1);
-    const u32x4 u0 = __builtin_nontemporal_load(pu);
-    const u32x4 u1 = __builtin_nontemporal_load(pu + 1);
-    const uint32_t gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-    const uint32_t uw[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+// Raw 16-byte loads of this thread's L units of a row (gate and, for SwiGLU,
+// up).  Units past the row end load the row's last unit instead, so every
+// load is issued unconditionally and all of them are in flight together; the
+// caller masks those units out.
+template <int ACT, int L>
+__device__ __forceinline__ void load_units(const uint16_t* __restrict__ xr, int64_t k_out, int units,
+                                           int tid, int T, u32x4 (&g)[L], u32x4 (&u)[L]) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < L; ++i) {
+    const int q0 = tid + i * T;
+    const int q = q0 < units ? q0 : units - 1;
+    g[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + 8 * (int64_t)q));
+    if constexpr (ACT == kActSwiglu)
+      u[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + k_out + 8 * (int64_t)q));
+  }
+}
+
+// The eight activation outputs of one unit from its raw words.
+template <int DT, int ACT>
+__device__ __forceinline__ void unit_values(const u32x4& g, const u32x4& u, float* y) {
+  const uint32_t w[4] = {g.x, g.y, g.z, g.w};
+  if constexpr (ACT == kActSwiglu) {
+    const uint32_t v[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
       float ga, gb, ua, ub;
-      unpack2<DT>(gw[i], ga, gb);
-      unpack2<DT>(uw[i], ua, ub);
+      unpack2<DT>(w[i], ga, gb);
+      unpack2<DT>(v[i], ua, ub);
       y[2 * i] = swiglu_f32(ga, ua);
       y[2 * i + 1] = swiglu_f32(gb, ub);
     }
   } else {
-    const u32x4* p = reinterpret_cast<const u32x4*>(xr + 16 * (int64_t)j);
-    const u32x4 a0 = __builtin_nontemporal_load(p);
-    const u32x4 a1 = __builtin_nontemporal_load(p + 1);
-    const uint32_t w[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float a, b;
-      unpack2<DT>(w[i], a, b);
-      if constexpr (ACT == kActRelu2) { a = relu2_f32(a); b = relu2_f32(b); }
-      y[2 * i] = a;
-      y[2 * i + 1] = b;
+    for (int i = 0; i < 4; ++i) {
+      float a0, a1;
+      unpack2<DT>(w[i], a0, a1);
+      if constexpr (ACT == kActRelu2) { a0 = relu2_f32(a0); a1 = relu2_f32(a1); }
+      y[2 * i] = a0;
+      y[2 * i + 1] = a1;
     }
   }
 }
@@ -83,9 +105,10 @@ __device__ __forceinline__ void load_block_scalar(const uint16_t* __restrict__ x
   }
 }
 
-// Block-wide max; every thread gets the result.  blockDim.x <= 256.
+// Block-wide max; every thread gets the result.  `red` holds one float per
+// wave; the caller separates reuses of `red` by a barrier.
 __device__ __forceinline__ float block_max(float v, float* red) {
-  float w = wave_max(v);
+  const float w = wave_max_dpp(v);
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   if (lane == 0) red[wid] = w;
   __syncthreads();
@@ -104,54 +127,195 @@ __device__ __forceinline__ float partials_max(const float* __restrict__ parts, i
   return m;
 }
 
-// Row kernel with the row cached in registers: NB blocks per thread, T
-// threads per row (blockDim.x = T rounded up to a wave).
-template <int DT, int ACT, int NB>
+// Block amax of a unit from its own 8 values and its pair lane's.
+__device__ __forceinline__ float unit_pair_max(const float* y) {
+  float m = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(y[e]));
+  return __builtin_fmaxf(m, dpp_f32<0xB1>(m));
+}
+
+// Encodes this thread's L units of a row.  Unit i of the two lanes of a pair
+// is one 16-block; the pair splits the block scales between them (the lane
+// of parity p evaluates the blocks of units i = p, p+2, ...) and exchanges
+// the encode factors, so each block's scale is computed once and each lane
+// stores the scale bytes of the blocks it evaluated.
+template <int L>
+__device__ __forceinline__ void encode_units(const float (&y)[L][8], const float (&am)[L], float g_enc,
+                                             float gd, int tid, int T, int units,
+                                             uint8_t* __restrict__ cr, uint8_t* __restrict__ sr,
+                                             float* __restrict__ scr) {
+  constexpr int J = (L + 1) / 2;
+  const int p = tid & 1;
+  const uint32_t pmask = 0u - (uint32_t)p;   // all ones on odd lanes
+  float enc_own[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int i_odd = (2 * j + 1 < L) ? 2 * j + 1 : 2 * j;
+    // bit select rather than a lane-dependent array index, which the compiler
+    // would turn into a memory access
+    const float amb = __uint_as_float((__float_as_uint(am[i_odd]) & pmask) |
+                                      (__float_as_uint(am[2 * j]) & ~pmask));
+    float c, enc;
+    const uint32_t sbyte = block_scale(amb, g_enc, gd, c, enc);
+    enc_own[j] = enc;
+    const int i = 2 * j + p;
+    const int q = tid + i * T;
+    if (i < L && q < units) {
+      sr[q >> 1] = (uint8_t)sbyte;
+      if (scr) scr[q >> 1] = c;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const float other = dpp_f32<0xB1>(enc_own[j]);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int i = 2 * j + b;
+      if (i >= L) continue;
+      const float enc = (b == p) ? enc_own[j] : other;
+      const int q = tid + i * T;
+      if (q < units)
+        __builtin_nontemporal_store(pack8_e2m1(y[i], enc), reinterpret_cast<uint32_t*>(cr + 4 * (int64_t)q));
+    }
+  }
+}
+
+// Row kernel with the row cached in registers: L units per thread, one row
+// per workgroup, blockDim.x a multiple of 64 (so unit pairs share a wave).
+template <int DT, int ACT, int L>
 __global__ void __launch_bounds__(kMaxThreads)
-quant_rows_fast(const uint16_t* __restrict__ x, int64_t k_out, int nb, int T,
-                uint8_t* __restrict__ codes, uint8_t* __restrict__ sf, float* __restrict__ g_dec,
-                float* __restrict__ scale_out, const float* __restrict__ parts, int64_t group_rows,
-                int nparts) {
+quant_rows_vec(const uint16_t* __restrict__ x, int64_t k_out, int units,
+               uint8_t* __restrict__ codes, uint8_t* __restrict__ sf, float* __restrict__ g_dec,
+               float* __restrict__ scale_out, const float* __restrict__ parts, int64_t group_rows,
+               int nparts) {
   __shared__ float red[kMaxThreads / 64];
   const int64_t row = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, T = blockDim.x;
   const int64_t k_in = (ACT == kActSwiglu) ? 2 * k_out : k_out;
   const uint16_t* xr = x + row * k_in;
-  float y[NB][16];
-  float am[NB];
+  u32x4 rg[L], ru[L];
+  load_units<ACT, L>(xr, k_out, units, tid, T, rg, ru);
+  float y[L][8];
+  float am[L];
   float tmax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int j = tid + i * T;
-    am[i] = 0.0f;
-    if (tid < T && j < nb) {
-      load_block_vec<DT, ACT>(xr, k_out, j, y[i]);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) am[i] = __builtin_fmaxf(am[i], __builtin_fabsf(y[i][e]));
-      tmax = __builtin_fmaxf(tmax, am[i]);
-    }
+  for (int i = 0; i < L; ++i) {
+    unit_values<DT, ACT>(rg[i], ru[i], y[i]);
+    const float m = unit_pair_max(y[i]);
+    am[i] = (tid + i * T < units) ? m : 0.0f;
+    tmax = __builtin_fmaxf(tmax, am[i]);
   }
   if (parts != nullptr) tmax = partials_max(parts, row, group_rows, nparts);
   const float amax = block_max(tmax, red);
   float g_enc, gd;
   global_scales(amax, g_enc, gd);
-  if (tid == 0 && (row % group_rows) == 0) g_dec[row / group_rows] = gd;
+  if (tid == 0) {
+    if (group_rows == 1) g_dec[row] = gd;
+    else if (row % group_rows == 0) g_dec[row / group_rows] = gd;
+  }
   uint8_t* cr = codes + row * (k_out / 2);
-  uint8_t* sr = sf + row * (int64_t)nb;
-  float* scr = scale_out ? scale_out + row * (int64_t)nb : nullptr;
+  uint8_t* sr = sf + row * (k_out / 16);
+  float* scr = scale_out ? scale_out + row * (k_out / 16) : nullptr;
+  encode_units<L>(y, am, g_enc, gd, tid, T, units, cr, sr, scr);
+}
+
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// silu of the two bf16 gates of one dword from the LDS table.  With
+// t = h - (kTabE0 << 7) per 16-bit half, a gate is in the table iff bits
+// 12..14 of t are clear (t in [0, 0x1000) for +, [0x8000, 0x9000) for -); the
+// entry is (t & 0xFFF) + 0x1000 * sign.  `acc` collects t for the miss test.
+__device__ __forceinline__ void silu_tab2(uint32_t w, const float* tab, uint32_t& acc, float& lo,
+                                          float& hi) {
+  const u16x2 k0 = {(uint16_t)(kTabE0 << 7), (uint16_t)(kTabE0 << 7)};
+  const uint32_t t = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, w) - k0);
+  acc |= t;
+  const uint32_t idx = (t & 0x0FFF0FFFu) | ((t >> 3) & 0x10001000u);
+  lo = tab[idx & 0xFFFFu];
+  hi = tab[idx >> 16];
+}
+
+// One row of the tabulated SwiGLU kernel from its raw gate/up words.
+template <int L>
+__device__ __forceinline__ void swiglu_tab_row(const u32x4 (&rg)[L], const u32x4 (&ru)[L],
+                                               const float* tab, float* red, int64_t row,
+                                               int64_t k_out, int units, uint8_t* __restrict__ codes,
+                                               uint8_t* __restrict__ sf, float* __restrict__ g_dec,
+                                               float* __restrict__ scale_out) {
+  const int tid = threadIdx.x, T = blockDim.x;
+  float y[L][8];
+  uint32_t miss = 0;
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int j = tid + i * T;
-    if (tid < T && j < nb) {
-      float c, enc;
-      const uint32_t s = block_scale(am[i], g_enc, gd, c, enc);
-      u32x2 o;
-      o.x = pack8_e2m1(&y[i][0], enc);
-      o.y = pack8_e2m1(&y[i][8], enc);
-      __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(cr + 8 * (int64_t)j));
-      sr[j] = (uint8_t)s;
-      if (scr) scr[j] = c;
+  for (int i = 0; i < L; ++i) {
+    const uint32_t gw[4] = {rg[i].x, rg[i].y, rg[i].z, rg[i].w};
+    const uint32_t uw[4] = {ru[i].x, ru[i].y, ru[i].z, ru[i].w};
+    uint32_t acc = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float slo, shi;
+      silu_tab2(gw[e], tab, acc, slo, shi);
+      y[i][2 * e] = slo * bf16_lo(uw[e]);
+      y[i][2 * e + 1] = shi * bf16_hi(uw[e]);
     }
+    if (tid + i * T < units) miss |= acc;   // padding units are never recomputed
+  }
+  if (miss & 0x70007000u) {   // a gate outside the table in this lane: evaluate directly
+#pragma unroll
+    for (int i = 0; i < L; ++i) unit_values<kBf16, kActSwiglu>(rg[i], ru[i], y[i]);
+  }
+  float am[L];
+  float tmax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const float m = unit_pair_max(y[i]);
+    am[i] = (tid + i * T < units) ? m : 0.0f;
+    tmax = __builtin_fmaxf(tmax, am[i]);
+  }
+  const float amax = block_max(tmax, red);
+  float g_enc, gd;
+  global_scales(amax, g_enc, gd);
+  if (tid == 0) g_dec[row] = gd;
+  uint8_t* cr = codes + row * (k_out / 2);
+  uint8_t* sr = sf + row * (k_out / 16);
+  float* scr = scale_out ? scale_out + row * (k_out / 16) : nullptr;
+  encode_units<L>(y, am, g_enc, gd, tid, T, units, cr, sr, scr);
+}
+
+// Persistent fused SwiGLU + per-token quantize for bf16 rows.  Rows rotate
+// through three register buffers: the loads of the next two rows are in
+// flight while a row is reduced and encoded.  Rows past the end re-load the
+// last row (never used), so loads stay unconditional.  red[0..2] belong to
+// the three buffers, so two barriers separate consecutive uses of one.
+template <int L>
+__global__ void __launch_bounds__(kTabThreads)
+swiglu_quant_tab(const uint16_t* __restrict__ x, int64_t rows, int64_t k_out, int units,
+                 uint8_t* __restrict__ codes, uint8_t* __restrict__ sf, float* __restrict__ g_dec,
+                 float* __restrict__ scale_out) {
+  __shared__ float tab[2 * kTabHalf];
+  __shared__ float red[3][kTabThreads / 64];
+  const int tid = threadIdx.x, T = blockDim.x;
+  for (int i = tid; i < 2 * kTabHalf; i += T) {
+    const uint32_t h = ((uint32_t)(i >= kTabHalf) << 15) | ((kTabE0 << 7) + (uint32_t)(i & (kTabHalf - 1)));
+    tab[i] = silu_f32(__uint_as_float(h << 16));
+  }
+  __syncthreads();
+
+  const int64_t G = gridDim.x;
+  auto rowptr = [&](int64_t r) { return x + (r < rows ? r : rows - 1) * 2 * k_out; };
+  u32x4 ag[L], au[L], bg[L], bu[L], cg[L], cu[L];
+  int64_t row = blockIdx.x;
+  load_units<kActSwiglu, L>(rowptr(row), k_out, units, tid, T, ag, au);
+  load_units<kActSwiglu, L>(rowptr(row + G), k_out, units, tid, T, bg, bu);
+  for (; row < rows; row += 3 * G) {
+    load_units<kActSwiglu, L>(rowptr(row + 2 * G), k_out, units, tid, T, cg, cu);
+    swiglu_tab_row<L>(ag, au, tab, red[0], row, k_out, units, codes, sf, g_dec, scale_out);
+    if (row + G >= rows) break;
+    load_units<kActSwiglu, L>(rowptr(row + 3 * G), k_out, units, tid, T, ag, au);
+    swiglu_tab_row<L>(bg, bu, tab, red[1], row + G, k_out, units, codes, sf, g_dec, scale_out);
+    if (row + 2 * G >= rows) break;
+    load_units<kActSwiglu, L>(rowptr(row + 4 * G), k_out, units, tid, T, bg, bu);
+    swiglu_tab_row<L>(cg, cu, tab, red[2], row + 2 * G, k_out, units, codes, sf, g_dec, scale_out);
   }
 }
 
@@ -216,37 +380,51 @@ group_amax_parts(const uint16_t* __restrict__ x, int64_t group_elems, int64_t ch
   if (threadIdx.x == 0) parts[g * nparts + p] = m;
 }
 
-template <int DT, int ACT, int NB>
-void launch_fast(const QuantArgs& a, int T, hipStream_t s) {
-  const int threads = ((T + 63) / 64) * 64;
-  hipLaunchKernelGGL((quant_rows_fast<DT, ACT, NB>), dim3((unsigned)a.rows), dim3(threads), 0, s,
-                     (const uint16_t*)a.x, a.k_out, (int)(a.k_out / 16), T, a.codes, a.sf, a.g_dec,
-                     a.scale_out, a.parts, a.group_rows, a.nparts);
+template <int DT, int ACT, int L>
+void launch_vec(const QuantArgs& a, int units, int threads, hipStream_t s) {
+  hipLaunchKernelGGL((quant_rows_vec<DT, ACT, L>), dim3((unsigned)a.rows), dim3(threads), 0, s,
+                     (const uint16_t*)a.x, a.k_out, units, a.codes, a.sf, a.g_dec, a.scale_out,
+                     a.parts, a.group_rows, a.nparts);
 }
 
 template <int DT, int ACT>
-void dispatch_nb(const QuantArgs& a, int nb_per_thread, int T, hipStream_t s) {
-  switch (nb_per_thread) {
-    case 1: launch_fast<DT, ACT, 1>(a, T, s); break;
-    case 2: launch_fast<DT, ACT, 2>(a, T, s); break;
-    case 3: launch_fast<DT, ACT, 3>(a, T, s); break;
-    case 4: launch_fast<DT, ACT, 4>(a, T, s); break;
-    case 5: launch_fast<DT, ACT, 5>(a, T, s); break;
-    case 6: launch_fast<DT, ACT, 6>(a, T, s); break;
-    case 7: launch_fast<DT, ACT, 7>(a, T, s); break;
-    default: launch_fast<DT, ACT, 8>(a, T, s); break;
+void dispatch_vec(const QuantArgs& a, int units, int L, int threads, hipStream_t s) {
+  switch (L) {
+    case 1: launch_vec<DT, ACT, 1>(a, units, threads, s); break;
+    case 2: launch_vec<DT, ACT, 2>(a, units, threads, s); break;
+    case 3: launch_vec<DT, ACT, 3>(a, units, threads, s); break;
+    case 4: launch_vec<DT, ACT, 4>(a, units, threads, s); break;
+    case 5: launch_vec<DT, ACT, 5>(a, units, threads, s); break;
+    case 6: launch_vec<DT, ACT, 6>(a, units, threads, s); break;
+    case 7: launch_vec<DT, ACT, 7>(a, units, threads, s); break;
+    case 8: launch_vec<DT, ACT, 8>(a, units, threads, s); break;
+    case 9: case 10: launch_vec<DT, ACT, 10>(a, units, threads, s); break;
+    case 11: case 12: launch_vec<DT, ACT, 12>(a, units, threads, s); break;
+    default: launch_vec<DT, ACT, kMaxUnits>(a, units, threads, s); break;
   }
 }
 
+void launch_tab(const QuantArgs& a, int units, int threads, hipStream_t s) {
+  const int64_t grid = a.rows < a.num_cus ? a.rows : a.num_cus;
+  hipLaunchKernelGGL((swiglu_quant_tab<kTabUnits>), dim3((unsigned)grid), dim3(threads), 0, s,
+                     (const uint16_t*)a.x, a.rows, a.k_out, units, a.codes, a.sf, a.g_dec, a.scale_out);
+}
+
+int round64(int64_t n) { return (int)(((n + 63) / 64) * 64); }
+
 template <int DT, int ACT>
 void launch_rows(const QuantArgs& a, hipStream_t s) {
-  const int64_t nb = a.k_out / 16;
-  const bool aligned = ((uintptr_t)a.x % 16 == 0) && ((uintptr_t)a.codes % 8 == 0);
-  const int64_t per = (nb + kMaxThreads - 1) / kMaxThreads;
-  if (aligned && per <= 8) {
-    const int nbt = (int)(per < 1 ? 1 : per);
-    const int T = (int)((nb + nbt - 1) / nbt);
-    dispatch_nb<DT, ACT>(a, nbt, T, s);
+  const int64_t units = a.k_out / 8;
+  const bool aligned = ((uintptr_t)a.x % 16 == 0) && ((uintptr_t)a.codes % 4 == 0);
+  if (DT == kBf16 && ACT == kActSwiglu && aligned && a.parts == nullptr && a.rows >= kTabMinRows &&
+      units <= (int64_t)kTabThreads * kTabUnits && a.num_cus > 0) {
+    launch_tab(a, (int)units, round64((units + kTabUnits - 1) / kTabUnits), s);
+    return;
+  }
+  if (aligned && units <= (int64_t)kMaxThreads * kMaxUnits) {
+    const int L = (int)((units + kMaxThreads - 1) / kMaxThreads);
+    const int threads = round64((units + L - 1) / L);
+    dispatch_vec<DT, ACT>(a, (int)units, L, threads, s);
   } else {
     hipLaunchKernelGGL((quant_rows_generic<DT, ACT>), dim3((unsigned)a.rows), dim3(kMaxThreads), 0,
                        s, (const uint16_t*)a.x, a.k_out, a.codes, a.sf, a.g_dec, a.scale_out,

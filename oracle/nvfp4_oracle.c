@@ -216,9 +216,12 @@ void oracle_quantize_block(const float* y, float g_enc, float g_dec, uint8_t* sf
   float sfd = (float)oracle_e4m3_decode(sf);     /* exact */
   float c = sfd * g_dec;
   float enc = (c == 0.0f) ? 0.0f : 1.0f / c;
+  /* A zero element always encodes to a zero code with its own sign.  This only
+     matters where 1/c overflows to +inf (c below 2^-128, rows whose amax is
+     under about 1e-34), where the product 0 * inf would be NaN. */
   for (int i = 0; i < 8; ++i) {
-    float v0 = y[2 * i] * enc;
-    float v1 = y[2 * i + 1] * enc;
+    float v0 = (y[2 * i] == 0.0f) ? y[2 * i] : y[2 * i] * enc;
+    float v1 = (y[2 * i + 1] == 0.0f) ? y[2 * i + 1] : y[2 * i + 1] * enc;
     codes8[i] = (uint8_t)(oracle_e2m1_encode(v0) | (oracle_e2m1_encode(v1) << 4));
   }
   *sf_out = sf;

@@ -177,3 +177,42 @@ def test_no_scale_output_and_empty(nv, oracle):
     _cmp(got, want)
     e = nv.quantize(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"))
     assert e["codes"].shape == (0, 32)
+
+
+def _one_gate_per_row(patterns: np.ndarray, torch_dtype):
+    """Rows of one 16-block whose SwiGLU output is silu(g) * 1 at position 0
+    and silu(0) * 1 = 0 elsewhere: the row amax, hence the stored global
+    1 / (2688 / amax), exposes |silu(g)| and the code exposes its sign."""
+    n = patterns.size
+    x = np.zeros((n, 32), np.uint16)
+    x[:, 0] = patterns
+    one = 0x3F80 if torch_dtype == torch.bfloat16 else 0x3C00
+    x[:, 16:] = one
+    return torch.from_numpy(x.view(np.int16)).view(torch_dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_swiglu_every_finite_gate_value(nv, oracle, dtype):
+    """silu over every finite 16-bit gate value: bf16 runs the tabulated path
+    (more than 1024 rows), fp16 the direct evaluation."""
+    p = np.arange(65536, dtype=np.uint32)
+    if dtype == torch.bfloat16:
+        finite = ((p >> 7) & 0xFF) != 0xFF
+    else:
+        finite = ((p >> 10) & 0x1F) != 0x1F
+    x = _one_gate_per_row(p[finite].astype(np.uint16), dtype)
+    want = oracle.quantize(x, act=1)
+    got = _gpu_quant(nv, x, "swiglu")
+    _cmp(got, want)
+
+
+@pytest.mark.parametrize("rows,k_out", [(1100, 272), (1030, 16384), (1024, 16), (1030, 24576)])
+def test_swiglu_tabulated_path_shapes(nv, oracle, rows, k_out):
+    """Persistent tabulated SwiGLU kernel: ragged last wave, three units per
+    lane, exactly the row threshold; every row compared."""
+    x32 = si.normal_f32((rows, 2 * k_out), 1.0, 96, 0, seed=rows + k_out,
+                        outlier_frac=0.01, outlier_scale=50.0)
+    x = torch.from_numpy(x32).to(torch.bfloat16)
+    want = oracle.quantize(x, act=1)
+    got = _gpu_quant(nv, x, "swiglu")
+    _cmp(got, want)

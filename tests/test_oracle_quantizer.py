@@ -172,6 +172,26 @@ def test_zero_and_constant_rows(oracle):
     assert np.all(q["codes"][2] == 0xFF) and np.all(q["sf"][2] == 0x7E)
 
 
+def test_row_whose_encode_factor_overflows(oracle):
+    """Row maximum 2^-133 (the smallest bf16 subnormal): 2688/amax overflows,
+    so g_enc = FLT_MAX and g_dec = 1/FLT_MAX rounds to 2^-128; the block scale
+    (2^-133/6)*FLT_MAX = 10923*2^-21 lies between the E4M3 subnormals 2*2^-9
+    and 3*2^-9 (nearer 3); c = 3*2^-137 is exact, 1/c overflows to +inf.  The
+    non-zero element saturates to code 7 and zero elements keep zero codes
+    with their own sign."""
+    x = np.zeros((1, 16), np.uint16)
+    x[0, 0] = 0x0001                 # +2^-133
+    x[0, 5] = 0x8000                 # -0
+    q = oracle.quantize(torch.from_numpy(x.view(np.int16)).view(torch.bfloat16))
+    assert q["g_dec"][0] == np.float32(2.0 ** -128)
+    assert q["sf"][0, 0] == 0x03
+    assert q["scale"][0, 0] == np.float32(3 * 2.0 ** -137)
+    nib = np.stack([q["codes"][0] & 0xF, q["codes"][0] >> 4], axis=1).reshape(-1)
+    want = np.zeros(16, np.uint8)
+    want[0], want[5] = 7, 8
+    assert nib.tolist() == want.tolist()
+
+
 def test_per_tensor_equals_per_row_when_row_maxima_agree(oracle):
     x = _random_rows(rows=8, k=128, seed=4, outliers=False).double()
     x[:, 5] = 1000.0                       # every row has the same maximum
