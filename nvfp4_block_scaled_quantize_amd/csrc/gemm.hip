@@ -18,8 +18,9 @@
 //    flight per lane), converts them with v_cvt_scalef32_pk_f16_fp4 and one
 //    packed FP16 multiply by the E4M3 scale, and feeds v_mfma_f32_16x16x32_f16
 //    with the (up to 16) activation rows as the other operand.  The activations
-//    are dequantized once per workgroup into LDS.  The four K quarters are
-//    summed in LDS in a fixed order (deterministic).
+//    are dequantized once per workgroup into LDS while the first weight chunks
+//    are in flight.  The four K quarters are summed in LDS in a fixed order
+//    (deterministic).
 //  * gemm_tiled (larger B, prefill): a prologue kernel writes the normalized
 //    FP16 activations once; the main kernel computes 256x256 output tiles with
 //    4 waves (128x128 each, v_mfma_f32_32x32x16_f16), staging FP16 activations
@@ -95,13 +96,25 @@ constexpr int kSkNsub = 2;        // 16-row subtiles per workgroup
 constexpr int kSkKs = 4;          // K quarters per workgroup
 constexpr int kSkRows = 16 * kSkNsub;
 constexpr int kSkPF = 8;          // 128-k chunks loaded per round per wave
+constexpr int kSkItems = 16;      // activation items (8 codes) per thread
+constexpr int kSkEarly = 2;       // weight chunks loaded before the activation prologue
 constexpr size_t kSkRedBytes = (size_t)kSkKs * kSkRows * 16 * sizeof(float);
-constexpr size_t kMaxLds = 160 * 1024;
 
-size_t skinny_lds_bytes(int64_t B, int64_t K) {
-  return (((size_t)B * (size_t)(K + 8) * 2 + 15) / 16) * 16 + kSkRedBytes;
-}
-
+// One workgroup = 8 waves = 2 sixteen-row weight subtiles x 4 K quarters.
+// Order of work, chosen against the memory latency chain of one workgroup:
+//  1. every thread issues the loads of its activation items (a few codes +
+//     combined scales; shared by all workgroups, so they hit L2), the global
+//     weight scale, and the weight loads of the first kSkEarly chunks;
+//  2. row maxima of the combined scales (wave reduction + LDS integer max),
+//     the per-row power of two, and the FP16 activations in LDS -- three
+//     barriers, which wait only for the issue of the few loads above (a wave
+//     whose weight loads are throttled by HBM would hold every barrier);
+//  3. the remaining weight loads of the round, then MFMAs chunk by chunk as the
+//     data arrives (in-order load counter);
+//  4. the four K quarters are summed in LDS in a fixed order.
+// A4: activation codes 4-byte aligned (dword loads), else byte loads.
+// NI: activation items (units of eight codes) per thread, >= B * ceil(K/8 / 512).
+template <bool A4, int NI>
 __global__ void __launch_bounds__(kSkThreads)
 gemm_skinny(const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
             const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_sf,
@@ -109,90 +122,132 @@ gemm_skinny(const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ float rs[16];
   __shared__ float rinv[16];
+  __shared__ uint32_t rmax[16];
   const int pitch = K + 8;   // halves; keeps consecutive activation rows 16 B apart in bank space
   _Float16* As = reinterpret_cast<_Float16*>(smem);
   float* red = reinterpret_cast<float*>(smem + (((size_t)B * pitch * 2 + 15) / 16) * 16);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int nsub = wave % kSkNsub, ks = wave / kSkNsub;
   const int r16 = lane & 15, g = lane >> 4;
   const int nrow = blockIdx.x * kSkRows + nsub * 16 + r16;
   const int64_t kb2 = K / 2, kb16 = K / 16;
   const int nchunks = (K + 127) >> 7;
+  if (tid < 16) rmax[tid] = 0u;
 
-  // 1. weight loads of the first round (issued before the activation work)
-  const bool nvalid = nrow < N;
-  const uint8_t* wr = w + (int64_t)(nvalid ? nrow : 0) * kb2;
-  const uint8_t* sr = w_sf + (int64_t)(nvalid ? nrow : 0) * kb16;
+  // 1a. this thread's activation items: item j is unit q8 = tid + 512 i (eight
+  //     codes) of row b, (b, i) running over (0, 0), (0, 1), ..., (0, ipr-1),
+  //     (1, 0), ... (wave-uniform counters).  Loads are unconditional: items
+  //     past the last row or the row end re-load a valid unit (masked later).
+  const int per_row = K / 8;
+  const int ipr = (per_row + kSkThreads - 1) / kSkThreads;
+  uint32_t acode[NI];
+  float ascl[NI];
+  {
+    int b = 0, i = 0;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int q8 = tid + kSkThreads * i;
+      const int bb = b < B ? b : B - 1;
+      const int qq = q8 < per_row ? q8 : 0;
+      const uint8_t* pa = a + (int64_t)bb * kb2 + 4 * (int64_t)qq;
+      acode[j] = A4 ? *reinterpret_cast<const uint32_t*>(pa) : load_u32_bytes(pa);
+      ascl[j] = a_scale[(int64_t)bb * kb16 + qq / 2];
+      if (++i == ipr) { i = 0; ++b; }
+    }
+  }
+  const float gw = *w_g;
+
+  // 1b. weight loads.  Rows past N re-load row N-1 (their outputs are not
+  //     stored); chunks past the end of K re-load chunk 0 and are skipped.
+  const uint8_t* wr = w + (int64_t)(nrow < N ? nrow : N - 1) * kb2;
+  const uint8_t* sr = w_sf + (int64_t)(nrow < N ? nrow : N - 1) * kb16;
   uint4 wc[kSkPF];
   uint32_t wsv[kSkPF];
-  auto load_round = [&](int c0) {
+  auto load_chunks = [&](int c0, int i0, int i1) {
 #pragma unroll
     for (int i = 0; i < kSkPF; ++i) {
+      if (i < i0 || i >= i1) continue;
       const int c = c0 + i * kSkKs;
-      const int k = c * 128 + 32 * g;
-      const bool v = nvalid && c < nchunks && k < K;
-      wc[i] = v ? *reinterpret_cast<const uint4*>(wr + k / 2) : make_uint4(0, 0, 0, 0);
-      wsv[i] = v ? (uint32_t)*reinterpret_cast<const uint16_t*>(sr + k / 16) : 0u;
+      const int k0 = c * 128 + 32 * g;
+      const int k = (c < nchunks && k0 < K) ? k0 : 0;
+      wc[i] = *reinterpret_cast<const uint4*>(wr + k / 2);
+      wsv[i] = (uint32_t)*reinterpret_cast<const uint16_t*>(sr + k / 16);
     }
   };
-  load_round(ks);
+  load_chunks(ks, 0, kSkEarly);
+  __syncthreads();   // rmax cleared
 
-  // 2. per-row power-of-two normalization of the activation scales
-  for (int b = wave; b < B; b += kSkThreads / 64) {
-    float m = 0.0f;
-    for (int64_t j = lane; j < kb16; j += 64) m = __builtin_fmaxf(m, a_scale[(int64_t)b * kb16 + j]);
-    m = wave_max(m);
-    if (lane == 0) {
-      const int e = row_exponent(m);
-      rs[b] = __builtin_ldexpf(1.0f, e);
-      rinv[b] = __builtin_ldexpf(1.0f, -e);
+  // 2. per-row power-of-two normalization: row max of the (non-negative)
+  //    combined scales as an integer max of their bits, per wave then in LDS
+  {
+    float cur = 0.0f;
+    int b = 0, i = 0;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const bool v = tid + kSkThreads * i < per_row;
+      cur = __builtin_fmaxf(cur, v ? ascl[j] : 0.0f);
+      if (i + 1 == ipr || j == NI - 1) {
+        if (b < B) {
+          const float m = wave_max_dpp(cur);
+          if (lane == 0) atomicMax(&rmax[b], __float_as_uint(m) & 0x7FFFFFFFu);
+        }
+        cur = 0.0f;
+      }
+      if (++i == ipr) { i = 0; ++b; }
+    }
+  }
+  __syncthreads();
+  if (tid < B) {
+    const int e = row_exponent(__uint_as_float(rmax[tid]));
+    rs[tid] = __builtin_ldexpf(1.0f, e);
+    rinv[tid] = __builtin_ldexpf(1.0f, -e);
+  }
+  __syncthreads();
+  {
+    int b = 0, i = 0;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int q8 = tid + kSkThreads * i;
+      if (b < B && q8 < per_row)
+        *reinterpret_cast<v8h*>(As + (int64_t)b * pitch + 8 * q8) = dequant8_act(acode[j], ascl[j] * rinv[b]);
+      if (++i == ipr) { i = 0; ++b; }
     }
   }
   __syncthreads();
 
-  // 3. activations -> FP16 in LDS, eight codes per item
-  const int per_row = K / 8;
-  for (int idx = tid; idx < B * per_row; idx += kSkThreads) {
-    const int b = idx / per_row, q8 = idx - b * per_row;
-    const uint32_t codes = load_u32_bytes(a + (int64_t)b * kb2 + 4 * (int64_t)q8);
-    const float c = a_scale[(int64_t)b * kb16 + q8 / 2] * rinv[b];
-    *reinterpret_cast<v8h*>(As + (int64_t)b * pitch + 8 * q8) = dequant8_act(codes, c);
-  }
-  __syncthreads();
-
-  // 4. stream the weights
+  // 3. stream the weights.  Batch columns past B read row B-1 of the LDS
+  //    activations; their outputs are never stored.
+  load_chunks(ks, kSkEarly, kSkPF);
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  const bool bvalid = r16 < B;
-  const _Float16* arow = As + (bvalid ? r16 : 0) * pitch;
-  const v8h zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int c0 = ks;; ) {
+  const _Float16* arow = As + (r16 < B ? r16 : B - 1) * pitch;
+  for (int c0 = ks;;) {
 #pragma unroll
     for (int i = 0; i < kSkPF; ++i) {
       const int c = c0 + i * kSkKs;
-      if (c < nchunks) {
+      if (c < nchunks) {   // wave-uniform
         const int k = c * 128 + 32 * g;
-        const bool kv = k < K;
-        const _Float16 s0 = e4m3_b0_f16(wsv[i]), s1 = e4m3_b1_f16(wsv[i]);
-        const uint32_t cw[4] = {wc[i].x, wc[i].y, wc[i].z, wc[i].w};
+        const bool kv = k < K;   // false only in a partial last chunk
+        v8h bf[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const v8h af = dequant8_f16(cw[m], m < 2 ? s0 : s1);
-          const v8h bf = (bvalid && kv) ? *reinterpret_cast<const v8h*>(arow + k + 8 * m) : zero8;
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, acc, 0, 0, 0);
-        }
+        for (int m = 0; m < 4; ++m) bf[m] = *reinterpret_cast<const v8h*>(arow + (kv ? k : 0) + 8 * m);
+        const _Float16 s0 = e4m3_b0_f16(wsv[i]), s1 = e4m3_b1_f16(wsv[i]);
+        const uint32_t cw[4] = {kv ? wc[i].x : 0u, kv ? wc[i].y : 0u, kv ? wc[i].z : 0u, kv ? wc[i].w : 0u};
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16(cw[m], m < 2 ? s0 : s1), bf[m], acc, 0, 0, 0);
       }
     }
     c0 += kSkPF * kSkKs;
     if (c0 >= nchunks) break;
-    load_round(c0);
+    load_chunks(c0, 0, kSkPF);
   }
 
-  // 5. sum the K quarters in a fixed order, scale, round to FP16
+  // 4. sum the K quarters in a fixed order, scale, round to FP16
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[(ks * kSkRows + nsub * 16 + 4 * g + r) * 16 + r16] = acc[r];
   __syncthreads();
-  const float gw = *w_g;
   for (int t = tid; t < 16 * kSkRows; t += kSkThreads) {
     const int b = t / kSkRows, nl = t % kSkRows;
     const int n = blockIdx.x * kSkRows + nl;
@@ -204,6 +259,27 @@ gemm_skinny(const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
     }
   }
 }
+
+typedef void (*SkinnyFn)(const uint8_t*, const float*, const uint8_t*, const uint8_t*, const float*,
+                         _Float16*, int, int, int);
+
+// The instantiation with the fewest activation items per thread covering ni.
+template <bool A4>
+SkinnyFn skinny_kernel_a(int ni) {
+  if (ni <= 1) return gemm_skinny<A4, 1>;
+  if (ni <= 2) return gemm_skinny<A4, 2>;
+  if (ni <= 4) return gemm_skinny<A4, 4>;
+  if (ni <= 8) return gemm_skinny<A4, 8>;
+  return gemm_skinny<A4, kSkItems>;
+}
+SkinnyFn skinny_kernel(bool a4, int ni) { return a4 ? skinny_kernel_a<true>(ni) : skinny_kernel_a<false>(ni); }
+
+size_t skinny_lds_bytes(int64_t B, int64_t K) {
+  return (((size_t)B * (size_t)(K + 8) * 2 + 15) / 16) * 16 + kSkRedBytes;
+}
+
+// Dynamic LDS budget of the skinny kernel (its static LDS is 192 bytes).
+constexpr size_t kSkinnyDynMax = 160 * 1024 - 1024;
 
 // ------------------------------------------------------------ tiled (prefill)
 
@@ -375,8 +451,6 @@ gemm_tiled(const _Float16* __restrict__ a16, const float* __restrict__ rowscale,
   }
 }
 
-// Dynamic LDS budget of the skinny kernel (its static LDS is 128 bytes).
-constexpr size_t kSkinnyDynMax = kMaxLds - 1024;
 
 // ------------------------------------------------------------ tiled, LDS-DMA pipeline
 //
@@ -716,7 +790,10 @@ gemm_tiled_pipe8(const _Float16* __restrict__ a16, const float* __restrict__ row
   }
 }
 
-bool use_skinny(int64_t B, int64_t K) { return B <= 16 && skinny_lds_bytes(B, K) <= kSkinnyDynMax; }
+bool use_skinny(int64_t B, int64_t K) {
+  const int64_t ipr = (K / 8 + kSkThreads - 1) / kSkThreads;
+  return B <= 16 && skinny_lds_bytes(B, K) <= kSkinnyDynMax && B * ipr <= kSkItems;
+}
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -732,8 +809,10 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, []() {
-    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_skinny),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSkinnyDynMax);
+    for (int a4 = 0; a4 < 2 && attr_err == hipSuccess; ++a4)
+      for (int ni = 1; ni <= kSkItems && attr_err == hipSuccess; ni *= 2)
+        attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(skinny_kernel(a4 != 0, ni)),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSkinnyDynMax);
     if (attr_err == hipSuccess)
       attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTiledLds);
@@ -744,8 +823,10 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   _Float16* y = reinterpret_cast<_Float16*>(g.y);
   if (use_skinny(g.B, g.K)) {
     const unsigned grid = (unsigned)((N + kSkRows - 1) / kSkRows);
-    hipLaunchKernelGGL(gemm_skinny, dim3(grid), dim3(kSkThreads), skinny_lds_bytes(B, K), s, g.a,
-                       g.a_scale, g.w, g.w_sf, g.w_g, y, B, N, K);
+    const int ni = B * ((K / 8 + kSkThreads - 1) / kSkThreads);
+    const SkinnyFn fn = skinny_kernel(((uintptr_t)g.a % 4) == 0, ni);
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(kSkThreads), skinny_lds_bytes(B, K), s, g.a, g.a_scale,
+                       g.w, g.w_sf, g.w_g, y, B, N, K);
     return hipGetLastError();
   }
   _Float16* a16 = reinterpret_cast<_Float16*>(g.workspace);
