@@ -21,11 +21,13 @@
 //    are dequantized once per workgroup into LDS while the first weight chunks
 //    are in flight.  The four K quarters are summed in LDS in a fixed order
 //    (deterministic).
-//  * gemm_tiled (larger B, prefill): a prologue kernel writes the normalized
-//    FP16 activations once; the main kernel computes 256x256 output tiles with
-//    4 waves (128x128 each, v_mfma_f32_32x32x16_f16), staging FP16 activations
-//    and packed FP4 weight codes + E4M3 bytes through double-buffered LDS;
-//    weights are dequantized in registers right before each MFMA.
+//  * gemm_wide (larger B, prefill, K % 64 == 0): a prologue kernel writes the
+//    normalized FP16 activations once; the main kernel computes 128 x 512
+//    output tiles with 8 waves (128 x 64 each, v_mfma_f32_32x32x16_f16),
+//    streaming FP16 activations, packed FP4 weight codes and E4M3 bytes from
+//    global memory straight into four LDS stages; weights are dequantized in
+//    registers right before each MFMA.  gemm_tiled (256 x 256 tiles, register
+//    staging) serves K % 64 != 0.
 //
 // K permutation: inside each MFMA group the hardware sums over all k of the
 // instruction, so the assignment of actual k values to MFMA k-slots is free as
@@ -454,24 +456,9 @@ gemm_tiled(const _Float16* __restrict__ a16, const float* __restrict__ rowscale,
 
 // ------------------------------------------------------------ tiled, LDS-DMA pipeline
 //
-// Same tile and arithmetic as gemm_tiled, with the operand movement rebuilt
-// for latency hiding: the FP16 activations, the FP4 weight codes and the
-// E4M3 bytes go straight from global memory into LDS with
-// global_load_lds_dwordx4 / _dword (no staging registers), three LDS stages
-// deep (two stages of loads in flight while one is consumed), one barrier per
-// 64-k stage, and the MFMA operands of the next k-substep are read and
-// dequantized while the current 16 MFMAs run.  Requires K % 64 == 0.
-
-#define NVFP4_LDS(p) ((__attribute__((address_space(3))) void*)(p))
-
-constexpr int kPStages = 3;
-constexpr int kPAChunk = kTM * 16 + 64;          // one 8-k column of 256 rows (+64 B skew)
-constexpr int kPWHalf = kTN * 16 + 64;           // one 32-k half of 256 weight rows (+skew)
-constexpr int kPAOff = 0;
-constexpr int kPWOff = 8 * kPAChunk;
-constexpr int kPSOff = kPWOff + 2 * kPWHalf;
-constexpr int kPStage = kPSOff + kTN * 4;
-constexpr size_t kPipeLds = 0;   // all LDS of the pipelined kernel is static
+// The operands go straight from global memory into LDS with
+// global_load_lds_dwordx4 / _dword (no staging registers), several LDS stages
+// deep, one barrier per 64-k stage.  Requires K % 64 == 0.
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4]=7 | lgkmcnt[11:8]=15 | vmcnt[5:4] in bits [15:14]).
@@ -502,206 +489,89 @@ __device__ __forceinline__ void dma4(const void* sbase, uint32_t vofs, uint32_t 
                :: "s"(lds), "v"(vofs), "s"(sbase) : "memory", "m0");
 }
 
-__global__ void __launch_bounds__(kTThreads)
-gemm_tiled_pipe(const _Float16* __restrict__ a16, const float* __restrict__ rowscale,
-                const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_sf,
-                const float* __restrict__ w_g, _Float16* __restrict__ y, int B, int N, int K,
-                int tiles_m, int tiles_n) {
-  // Three stage buffers; the stage loop is unrolled by three so that every
-  // buffer is named statically.
-  __shared__ __attribute__((aligned(16))) unsigned char lds0[kPStage];
-  __shared__ __attribute__((aligned(16))) unsigned char lds1[kPStage];
-  __shared__ __attribute__((aligned(16))) unsigned char lds2[kPStage];
+constexpr int kP2Threads = 512;
+
+// 128 x 512 output tiles, eight waves side by side in N (128 x 64 each: four
+// 32-row x two 32-column v_mfma_f32_32x32x16_f16 blocks), four LDS stages
+// (three in flight).  Per 64-k stage the tile needs 16 KB of FP16 activations
+// and 16 KB of FP4 weights + 2 KB of E4M3 bytes -- about a sixth fewer bytes
+// per MAC than 256 x 256, because the weights are the cheap operand -- and the
+// smaller stage leaves room for the fourth buffer.  LDS layouts, chosen so
+// that every copy instruction reads whole row segments and the MFMA operand
+// reads are free of bank conflicts for both 8-lane (128 B) and 16-lane
+// (256 B) groups:
+//   A: blocks of 8 rows x 128 B; 16-byte chunk c of row r sits at position
+//      c ^ (r & 7) ^ ((r >> 3) & 1) of its row;
+//   W: 32 B per row; chunk h of row n at position h ^ (((n >> 2) ^ (n >> 3)) & 1).
+// Workgroup order: each XCD takes 64 consecutive tiles, walked 4 M-tiles at a
+// time, so its 32 resident workgroups share 4 activation row stripes and 8
+// weight column stripes in its L2.
+constexpr int kXM = 128, kXN = 512;
+constexpr int kXAOff = 0;                          // A: 128 rows x 128 B
+constexpr int kXWOff = kXAOff + kXM * 128;         // W: 512 rows x 32 B
+constexpr int kXSOff = kXWOff + kXN * 32;          // S: 512 rows x 4 B
+constexpr int kXStage = kXSOff + kXN * 4;
+
+__global__ void __launch_bounds__(kP2Threads)
+gemm_wide(const _Float16* __restrict__ a16, const float* __restrict__ rowscale,
+          const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_sf,
+          const float* __restrict__ w_g, _Float16* __restrict__ y, int B, int N, int K,
+          int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds0[kXStage];
+  __shared__ __attribute__((aligned(16))) unsigned char lds1[kXStage];
+  __shared__ __attribute__((aligned(16))) unsigned char lds2[kXStage];
+  __shared__ __attribute__((aligned(16))) unsigned char lds3[kXStage];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // N slice of 64 columns
   const int l32 = lane & 31, h = lane >> 5;
-  // XCD-aware order: consecutive workgroup ids land on different XCDs, so
-  // give each XCD a contiguous run of tiles (it then shares A rows in its L2).
   const int ntiles = tiles_m * tiles_n;
-  int tile = blockIdx.x;
-  if (ntiles % 8 == 0) tile = (tile % 8) * (ntiles / 8) + tile / 8;
-  const int tm = tile / tiles_n, tn = tile % tiles_n;
-  const int m0 = tm * kTM, n0 = tn * kTN;
+  int tm, tn;
+  {
+    const int t = blockIdx.x;
+    if (ntiles % 512 == 0 && tiles_m % 4 == 0 && tiles_n % 16 == 0) {
+      // groups of 64 tiles (4 M-tiles x 16 N-tiles, N-tiles outer), one group
+      // per XCD at a time (consecutive ids go to different XCDs)
+      const int xcd = t % 8, l = t / 8 % 64, grp = t / 512;
+      const int g = grp * 8 + xcd;
+      const int lm = l % 4, ln = l / 4;
+      const int groups_n = tiles_n / 16;
+      tm = (g / groups_n) * 4 + lm;
+      tn = (g % groups_n) * 16 + ln;
+    } else {
+      tm = t / tiles_n;
+      tn = t % tiles_n;
+    }
+  }
+  const int m0 = tm * kXM, n0 = tn * kXN;
   const int nsteps = K / kTK;
 
-  // per-lane 32-bit byte offsets of this wave's DMA sources (rows clamped to
-  // the matrix; clamped rows only feed outputs that are never stored)
-  uint32_t aofs[8], wofs[2], sofs;
-  int alds[8], wlds[2];
+  // DMA work of this wave per stage: A blocks 2w, 2w+1 (8 rows each), W rows
+  // 64w .. 64w+63 (two copies of 32 rows), E4M3 bytes of rows 64w .. 64w+63.
+  uint32_t aofs[2], wofs[2], sofs;
+  int alds[2], wlds[2], slds;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int i = wave * 8 + j, c = i >> 2, q = i & 3;
-    int r = m0 + 64 * q + lane;
-    r = r < B ? r : B - 1;
-    aofs[j] = (uint32_t)r * (uint32_t)K * 2u + 16u * c;
-    alds[j] = kPAOff + c * kPAChunk + q * 1024;
+  for (int j = 0; j < 2; ++j) {
+    const int blk = wave * 2 + j, r8 = lane >> 3, c = (lane & 7) ^ r8 ^ (blk & 1);
+    {
+      int r = m0 + 8 * blk + r8;
+      r = r < B ? r : B - 1;
+      aofs[j] = (uint32_t)r * (uint32_t)K * 2u + 16u * c;
+      alds[j] = kXAOff + (wave * 2 + j) * 1024;
+    }
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int i = wave * 2 + j, hh = i >> 2, q = i & 3;
-    int r = n0 + 64 * q + lane;
+    const int rl = 64 * wave + 32 * j + (lane >> 1);
+    int r = n0 + rl;
     r = r < N ? r : N - 1;
-    wofs[j] = (uint32_t)r * (uint32_t)(K / 2) + 16u * hh;
-    wlds[j] = kPWOff + hh * kPWHalf + q * 1024;
+    wofs[j] = (uint32_t)r * (uint32_t)(K / 2) + 16u * ((lane & 1) ^ (((rl >> 2) ^ (rl >> 3)) & 1));
+    wlds[j] = kXWOff + (wave * 2 + j) * 1024;
   }
   {
     int r = n0 + 64 * wave + lane;
     r = r < N ? r : N - 1;
     sofs = (uint32_t)r * (uint32_t)(K / 16);
-  }
-  const int slds = kPSOff + wave * 256;
-  const unsigned char* abase = reinterpret_cast<const unsigned char*>(a16);
-
-  auto issue = [&](unsigned char* buf, int st) {
-    const int k0 = st * kTK;
-    const unsigned char* ab = abase + (size_t)k0 * 2;
-    const uint8_t* wb = w + k0 / 2;
-    const uint8_t* sb = w_sf + k0 / 16;
-    const uint32_t l0 = lds_addr(buf);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) dma16(ab, aofs[j], l0 + alds[j]);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) dma16(wb, wofs[j], l0 + wlds[j]);
-    dma4(sb, sofs, l0 + slds);
-  };
-  constexpr int kLoadsPerStage = 11;
-
-  v16f acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  auto compute = [&](const unsigned char* st) {
-    uint4 wcode[4];
-    v2h wsc[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int nl = wn * 128 + nt * 32 + l32;
-      wcode[nt] = *reinterpret_cast<const uint4*>(st + kPWOff + h * kPWHalf + nl * 16);
-      const uint32_t sw = *reinterpret_cast<const uint32_t*>(st + kPSOff + nl * 4) >> (16 * h);
-      wsc[nt][0] = e4m3_b0_f16(sw);
-      wsc[nt][1] = e4m3_b1_f16(sw);
-    }
-    v8h af[2][4], bf[2][4];
-    auto load_a = [&](int m, v8h* dst) {
-#pragma unroll
-      for (int bt = 0; bt < 4; ++bt) {
-        const int rl = wm * 128 + bt * 32 + l32;
-        dst[bt] = *reinterpret_cast<const v8h*>(st + kPAOff + (4 * h + m) * kPAChunk + rl * 16);
-      }
-    };
-    auto deq_w = [&](int m, v8h* dst) {
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const uint32_t cw = (m == 0) ? wcode[nt].x : (m == 1) ? wcode[nt].y : (m == 2) ? wcode[nt].z : wcode[nt].w;
-        dst[nt] = dequant8_f16(cw, wsc[nt][m >> 1]);
-      }
-    };
-    load_a(0, af[0]);
-    deq_w(0, bf[0]);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int cur = m & 1;
-      if (m < 3) {
-        // operands of the next k-substep, overlapped with this substep's MFMAs
-        load_a(m + 1, af[cur ^ 1]);
-        deq_w(m + 1, bf[cur ^ 1]);
-      }
-#pragma unroll
-      for (int bt = 0; bt < 4; ++bt)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          acc[bt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][bt], bf[cur][nt], acc[bt][nt], 0, 0, 0);
-    }
-  };
-  // one 64-k stage: wait for its DMA, barrier, start stage s+2's DMA, compute
-  auto step = [&](const unsigned char* cur, unsigned char* next2, int s) {
-    if (s + 1 < nsteps) wait_vmcnt_le<kLoadsPerStage>();
-    else wait_vmcnt_le<0>();
-    __builtin_amdgcn_s_barrier();
-    if (s + 2 < nsteps) issue(next2, s + 2);
-    compute(cur);
-  };
-
-  issue(lds0, 0);
-  if (nsteps > 1) issue(lds1, 1);
-  for (int s = 0; s < nsteps; s += 3) {
-    step(lds0, lds2, s);
-    if (s + 1 < nsteps) step(lds1, lds0, s + 1);
-    if (s + 2 < nsteps) step(lds2, lds1, s + 2);
-  }
-
-  const float gw = *w_g;
-#pragma unroll
-  for (int bt = 0; bt < 4; ++bt) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = m0 + wm * 128 + bt * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-      if (row >= B) continue;
-      const float rsc = rowscale[row] * gw;
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int col = n0 + wn * 128 + nt * 32 + l32;
-        if (col < N) y[(int64_t)row * N + col] = (_Float16)(acc[bt][nt][r] * rsc);
-      }
-    }
-  }
-}
-
-// Eight-wave variant: the 256x256 tile is split into 2 x 4 wave tiles of
-// 128 x 64, so each wave holds 128 accumulators and two waves share a SIMD;
-// the hardware then overlaps one wave's LDS reads and dequantization with the
-// other wave's MFMAs.  Same LDS stages and DMA as gemm_tiled_pipe.
-constexpr int kP2Threads = 512;
-
-__global__ void __launch_bounds__(kP2Threads)
-gemm_tiled_pipe8(const _Float16* __restrict__ a16, const float* __restrict__ rowscale,
-                 const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_sf,
-                 const float* __restrict__ w_g, _Float16* __restrict__ y, int B, int N, int K,
-                 int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds0[kPStage];
-  __shared__ __attribute__((aligned(16))) unsigned char lds1[kPStage];
-  __shared__ __attribute__((aligned(16))) unsigned char lds2[kPStage];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;          // 2 x 4 waves of 128 x 64
-  const int l32 = lane & 31, h = lane >> 5;
-  const int ntiles = tiles_m * tiles_n;
-  int tile = blockIdx.x;
-  if (ntiles % 8 == 0) tile = (tile % 8) * (ntiles / 8) + tile / 8;
-  const int tm = tile / tiles_n, tn = tile % tiles_n;
-  const int m0 = tm * kTM, n0 = tn * kTN;
-  const int nsteps = K / kTK;
-
-  // DMA work of this wave per stage: 4 of the 32 A copies, 1 of the 8 W
-  // copies, and (waves 0..3) 1 of the 4 scale copies.
-  uint32_t aofs[4], wofs, sofs;
-  int alds[4], wlds, slds;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = wave * 4 + j, c = i >> 2, q = i & 3;
-    int r = m0 + 64 * q + lane;
-    r = r < B ? r : B - 1;
-    aofs[j] = (uint32_t)r * (uint32_t)K * 2u + 16u * c;
-    alds[j] = kPAOff + c * kPAChunk + q * 1024;
-  }
-  {
-    const int hh = wave >> 2, q = wave & 3;
-    int r = n0 + 64 * q + lane;
-    r = r < N ? r : N - 1;
-    wofs = (uint32_t)r * (uint32_t)(K / 2) + 16u * hh;
-    wlds = kPWOff + hh * kPWHalf + q * 1024;
-  }
-  const bool sdma = wave < 4;
-  {
-    int r = n0 + 64 * (wave & 3) + lane;
-    r = r < N ? r : N - 1;
-    sofs = (uint32_t)r * (uint32_t)(K / 16);
-    slds = kPSOff + (wave & 3) * 256;
+    slds = kXSOff + wave * 256;
   }
   const unsigned char* abase = reinterpret_cast<const unsigned char*>(a16);
 
@@ -710,10 +580,12 @@ gemm_tiled_pipe8(const _Float16* __restrict__ a16, const float* __restrict__ row
     const unsigned char* ab = abase + (size_t)k0 * 2;
     const uint32_t l0 = lds_addr(buf);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(ab, aofs[j], l0 + alds[j]);
-    dma16(w + k0 / 2, wofs, l0 + wlds);
-    if (sdma) dma4(w_sf + k0 / 16, sofs, l0 + slds);
+    for (int j = 0; j < 2; ++j) dma16(ab, aofs[j], l0 + alds[j]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16(w + k0 / 2, wofs[j], l0 + wlds[j]);
+    dma4(w_sf + k0 / 16, sofs, l0 + slds);
   };
+  constexpr int kLoads = 5;   // per wave per stage
 
   v16f acc[4][2];
 #pragma unroll
@@ -723,14 +595,18 @@ gemm_tiled_pipe8(const _Float16* __restrict__ a16, const float* __restrict__ row
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  auto a_off = [](int rl, int c) {
+    return kXAOff + (rl >> 3) * 1024 + 16 * (8 * (rl & 7) + (c ^ (rl & 7) ^ ((rl >> 3) & 1)));
+  };
+
   auto compute = [&](const unsigned char* st) {
     uint4 wcode[2];
     v2h wsc[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const int nl = wn * 64 + nt * 32 + l32;
-      wcode[nt] = *reinterpret_cast<const uint4*>(st + kPWOff + h * kPWHalf + nl * 16);
-      const uint32_t sw = *reinterpret_cast<const uint32_t*>(st + kPSOff + nl * 4) >> (16 * h);
+      const int nl = wave * 64 + nt * 32 + l32;
+      wcode[nt] = *reinterpret_cast<const uint4*>(st + kXWOff + nl * 32 + 16 * (h ^ (((nl >> 2) ^ (nl >> 3)) & 1)));
+      const uint32_t sw = *reinterpret_cast<const uint32_t*>(st + kXSOff + nl * 4) >> (16 * h);
       wsc[nt][0] = e4m3_b0_f16(sw);
       wsc[nt][1] = e4m3_b1_f16(sw);
     }
@@ -738,10 +614,7 @@ gemm_tiled_pipe8(const _Float16* __restrict__ a16, const float* __restrict__ row
     for (int m = 0; m < 4; ++m) {
       v8h af[4], bf[2];
 #pragma unroll
-      for (int bt = 0; bt < 4; ++bt) {
-        const int rl = wm * 128 + bt * 32 + l32;
-        af[bt] = *reinterpret_cast<const v8h*>(st + kPAOff + (4 * h + m) * kPAChunk + rl * 16);
-      }
+      for (int bt = 0; bt < 4; ++bt) af[bt] = *reinterpret_cast<const v8h*>(st + a_off(bt * 32 + l32, 4 * h + m));
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const uint32_t cw = (m == 0) ? wcode[nt].x : (m == 1) ? wcode[nt].y : (m == 2) ? wcode[nt].z : wcode[nt].w;
@@ -754,23 +627,25 @@ gemm_tiled_pipe8(const _Float16* __restrict__ a16, const float* __restrict__ row
           acc[bt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[bt], bf[nt], acc[bt][nt], 0, 0, 0);
     }
   };
-  auto step = [&](const unsigned char* cur, unsigned char* next2, int s) {
-    if (s + 1 < nsteps) {
-      if (sdma) wait_vmcnt_le<6>(); else wait_vmcnt_le<5>();
-    } else {
-      wait_vmcnt_le<0>();
-    }
+  // one 64-k stage: wait for its DMA (stages s+1, s+2 may stay in flight),
+  // barrier, start stage s+3's DMA into the buffer freed by stage s-1, compute
+  auto step = [&](const unsigned char* cur, unsigned char* next3, int s) {
+    if (s + 2 < nsteps) wait_vmcnt_le<2 * kLoads>();
+    else if (s + 1 < nsteps) wait_vmcnt_le<kLoads>();
+    else wait_vmcnt_le<0>();
     __builtin_amdgcn_s_barrier();
-    if (s + 2 < nsteps) issue(next2, s + 2);
+    if (s + 3 < nsteps) issue(next3, s + 3);
     compute(cur);
   };
 
   issue(lds0, 0);
   if (nsteps > 1) issue(lds1, 1);
-  for (int s = 0; s < nsteps; s += 3) {
-    step(lds0, lds2, s);
+  if (nsteps > 2) issue(lds2, 2);
+  for (int s = 0; s < nsteps; s += 4) {
+    step(lds0, lds3, s);
     if (s + 1 < nsteps) step(lds1, lds0, s + 1);
     if (s + 2 < nsteps) step(lds2, lds1, s + 2);
+    if (s + 3 < nsteps) step(lds3, lds2, s + 3);
   }
 
   const float gw = *w_g;
@@ -778,12 +653,12 @@ gemm_tiled_pipe8(const _Float16* __restrict__ a16, const float* __restrict__ row
   for (int bt = 0; bt < 4; ++bt) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = m0 + wm * 128 + bt * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+      const int row = m0 + bt * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
       if (row >= B) continue;
       const float rsc = rowscale[row] * gw;
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const int col = n0 + wn * 64 + nt * 32 + l32;
+        const int col = n0 + wave * 64 + nt * 32 + l32;
         if (col < N) y[(int64_t)row * N + col] = (_Float16)(acc[bt][nt][r] * rsc);
       }
     }
@@ -799,6 +674,7 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
 
+// Workspace of the tiled paths: [FP16 activations] [row powers of two].
 size_t gemm_workspace_bytes(int64_t B, int64_t N, int64_t K) {
   (void)N;
   if (use_skinny(B, K)) return 0;
@@ -829,16 +705,17 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
                        g.w, g.w_sf, g.w_g, y, B, N, K);
     return hipGetLastError();
   }
-  _Float16* a16 = reinterpret_cast<_Float16*>(g.workspace);
-  float* rowscale = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(g.workspace) +
-                                             align256((size_t)B * (size_t)K * 2));
+  unsigned char* ws = reinterpret_cast<unsigned char*>(g.workspace);
+  _Float16* a16 = reinterpret_cast<_Float16*>(ws);
+  float* rowscale = reinterpret_cast<float*>(ws + align256((size_t)B * (size_t)K * 2));
   hipLaunchKernelGGL(a_to_f16_rows, dim3((unsigned)B), dim3(256), 0, s, g.a, g.a_scale, a16,
                      rowscale, K);
-  const int tiles_m = (B + kTM - 1) / kTM, tiles_n = (N + kTN - 1) / kTN;
-  if (K % kTK == 0) {
-    hipLaunchKernelGGL(gemm_tiled_pipe8, dim3((unsigned)(tiles_m * tiles_n)), dim3(kP2Threads),
-                       kPipeLds, s, a16, rowscale, g.w, g.w_sf, g.w_g, y, B, N, K, tiles_m, tiles_n);
+  if (K % kTK == 0 && ((uintptr_t)g.w_sf % 4) == 0) {
+    const int wtm = (B + kXM - 1) / kXM, wtn = (N + kXN - 1) / kXN;
+    hipLaunchKernelGGL(gemm_wide, dim3((unsigned)(wtm * wtn)), dim3(kP2Threads), 0, s, a16,
+                       rowscale, g.w, g.w_sf, g.w_g, y, B, N, K, wtm, wtn);
   } else {
+    const int tiles_m = (B + kTM - 1) / kTM, tiles_n = (N + kTN - 1) / kTN;
     hipLaunchKernelGGL(gemm_tiled, dim3((unsigned)(tiles_m * tiles_n)), dim3(kTThreads), kTiledLds,
                        s, a16, rowscale, g.w, g.w_sf, g.w_g, y, B, N, K, tiles_n);
   }
