@@ -150,7 +150,7 @@ size_t nvfp4_gemm_workspace_size(int64_t B, int64_t N, int64_t K);
  * by their sum when norm_topk_prob, times routed_scaling.
  * Requires experts % n_group == 0, 1 <= topk_group <= n_group,
  * 1 <= top_k <= topk_group * experts / n_group, top_k <= 16, experts <= 256,
- * hidden % 32 == 0, inter % 32 == 0, tokens <= 16384; x, w1, w2 16-byte
+ * hidden % 64 == 0, inter % 64 == 0, inter <= 8192, tokens <= 2^24; x, w1, w2 16-byte
  * aligned, out 8-byte aligned, block scales 2-byte aligned (EINVAL otherwise).
  */
 int32_t nvfp4_moe_w4a16(const float* router_logits, const float* correction_bias, const void* x,

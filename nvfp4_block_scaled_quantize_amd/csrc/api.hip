@@ -60,7 +60,7 @@ const char* nvfp4_status_string(int32_t status) {
 size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t k, int64_t group_rows) {
   if (rows <= 0 || k <= 0 || group_rows <= 1 || rows % group_rows != 0) return 0;
   const int np = nvfp4::quant_num_parts(group_rows * k);
-  return (size_t)(rows / group_rows) * (size_t)np * sizeof(float);
+  return (size_t)(rows / group_rows) * (size_t)(np + 1) * sizeof(float);
 }
 
 static int32_t quantize_common(const void* x, int32_t dtype, int64_t rows, int64_t k_out,
@@ -143,13 +143,15 @@ int32_t nvfp4_moe_w4a16(const float* router_logits, const float* correction_bias
                         int32_t top_k, int32_t hidden, int32_t inter, int32_t n_group,
                         int32_t topk_group, int32_t norm_topk_prob, float routed_scaling,
                         void* workspace, size_t workspace_bytes, void* stream) {
-  if (tokens < 0 || experts <= 0 || experts > 256 || n_group <= 0 || experts % n_group != 0)
+  if (tokens < 0 || tokens > (1 << 24) || experts <= 0 || experts > 256 || n_group <= 0 ||
+      experts % n_group != 0)
     return NVFP4_EINVAL;
   const int gsize = experts / n_group;
   if (topk_group < 1 || topk_group > n_group || top_k < 1 || top_k > 16 ||
       top_k > topk_group * gsize)
     return NVFP4_EINVAL;
-  if (hidden <= 0 || inter <= 0 || hidden % 32 != 0 || inter % 32 != 0) return NVFP4_EINVAL;
+  if (hidden <= 0 || inter <= 0 || hidden % 64 != 0 || inter % 64 != 0 || inter > 8192)
+    return NVFP4_EINVAL;
   if (tokens == 0) return NVFP4_OK;
   if (!router_logits || !correction_bias || !x || !w1 || !w1_sf || !w1_g || !w2 || !w2_sf ||
       !w2_g || !out)
@@ -165,7 +167,8 @@ int32_t nvfp4_moe_w4a16(const float* router_logits, const float* correction_bias
   if (ds != NVFP4_OK) return ds;
   nvfp4::MoeArgs m{router_logits, correction_bias, x, w1, w1_sf, w1_g, w2, w2_sf, w2_g, out,
                    topk_ids_out, topk_w_out, tokens, experts, top_k, hidden, inter, n_group,
-                   topk_group, norm_topk_prob ? 1 : 0, routed_scaling, workspace, workspace_bytes};
+                   topk_group, norm_topk_prob ? 1 : 0, routed_scaling, workspace, workspace_bytes,
+                   current_device()->num_cus};
   return hip_status(nvfp4::launch_moe(m, (hipStream_t)stream));
 }
 

@@ -64,6 +64,7 @@ struct MoeArgs {
   float scaling;
   void* workspace;
   size_t workspace_bytes;
+  int num_cus;         // compute units of the current device (work split)
 };
 
 size_t moe_workspace_bytes(int tokens, int experts, int top_k, int hidden, int inter);

@@ -3,57 +3,63 @@
 // group-top-k routing with a correction bias, ReLU^2, NVFP4 fc1/fc2 with
 // per-expert FP32 global scales), for gfx950.
 //
-// Four launches, all deterministic (no floating-point atomics):
+// Five launches, all deterministic (no floating-point atomics):
 //  1. route      : one wave per token.  Lanes hold experts; sigmoid scores
 //                  (the same binary32 exp as the quantizer), biased scores,
 //                  group scores = sum of the group's two best, repeated wave
 //                  argmax for the kept groups and the top-k experts (ties to
 //                  the lower index), weights normalized in rank order.
-//  2. fc1        : grid (inter/128, experts).  Each workgroup finds the pairs
-//                  (token, rank) routed to its expert by a ballot scan of the
-//                  routing table in pair order, then computes
-//                  h = relu(x . W1^T * g1)^2 for 128 weight rows with
-//                  v_mfma_f32_32x32x16_f16 (weights dequantized in registers,
-//                  exact in FP16; token rows gathered from x as the other
-//                  operand).  h is stored in fp32 per pair, and the largest h
-//                  of each pair is folded into a per-pair maximum (integer
-//                  max on the fp32 bits: order independent).
-//  3. fc2        : grid (hidden/128, experts).  Same structure on h, which is
+//  2. lists      : one workgroup per expert writes the pairs (token, rank)
+//                  routed to it, in pair order, and their count.
+//  3. fc1        : grid (inter/256, experts), 8 waves x 32 weight rows.
+//                  Computes h = relu(x . W1^T * g1)^2 with
+//                  v_mfma_f32_16x16x32_f16: weights dequantized in registers
+//                  (exact in FP16) and streamed one 256-k chunk ahead, the
+//                  expert's tokens gathered from x into LDS in passes of 64.
+//                  h is stored in fp32 per pair, and the largest h of each
+//                  pair is folded into a per-pair maximum (integer max on the
+//                  fp32 bits: order independent).
+//  4. fc2        : grid (hidden/256, experts).  Same structure on h, which is
 //                  converted to FP16 after scaling by 2^-e (e = exponent of
 //                  the pair's maximum, so no pair can overflow FP16);
 //                  o = h . W2^T * g2 * 2^e, stored in fp32 per pair.
-//  4. combine    : out[t] = sum_j w[t,j] * o[t*top_k + j] in rank order, FP16.
+//  5. combine    : out[t] = sum_j w[t,j] * o[t*top_k + j] in rank order, FP16.
 #include "device_common.h"
 #include "internal.h"
-
-#include <mutex>
 
 namespace nvfp4 {
 
 namespace {
 
-constexpr int kFcThreads = 256;        // 4 waves x 32 weight rows
-constexpr int kFcRows = 128;
-constexpr int kTokTiles = 4;           // token tiles of 32 held in registers per pass
-
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct MoeWs {
-  int32_t* ids;
-  float* wts;
-  uint32_t* pmax;
-  float* h;
-  float* o;
+  int32_t* ids;      // [P] expert of each pair
+  float* wts;        // [P] its weight
+  uint32_t* pmax;    // [P] largest h of the pair (fp32 bits)
+  int32_t* counts;   // [E] pairs per expert
+  int32_t* plists;   // [E, T] pairs of each expert
+  int32_t* tlists;   // [E, T] their tokens
+  int32_t* etile;    // [P, nt1] exponent of each fc1 row tile's largest h
+  _Float16* h;       // [P, inter] scaled per fc1 row tile
+  float* o;          // [P, hidden]
 };
 
-MoeWs carve(void* base, int P, int hidden, int inter) {
+int fc1_tiles(int inter) { return (inter + 255) / 256; }
+
+MoeWs carve(void* base, int T, int E, int P, int hidden, int inter) {
   unsigned char* p = reinterpret_cast<unsigned char*>(base);
   MoeWs w;
   w.ids = reinterpret_cast<int32_t*>(p); p += align256((size_t)P * 4);
   w.wts = reinterpret_cast<float*>(p); p += align256((size_t)P * 4);
   w.pmax = reinterpret_cast<uint32_t*>(p); p += align256((size_t)P * 4);
-  w.h = reinterpret_cast<float*>(p); p += align256((size_t)P * inter * 4);
+  w.counts = reinterpret_cast<int32_t*>(p); p += align256((size_t)E * 4);
+  w.plists = reinterpret_cast<int32_t*>(p); p += align256((size_t)E * T * 4);
+  w.tlists = reinterpret_cast<int32_t*>(p); p += align256((size_t)E * T * 4);
+  w.etile = reinterpret_cast<int32_t*>(p); p += align256((size_t)P * fc1_tiles(inter) * 4);
+  w.h = reinterpret_cast<_Float16*>(p); p += align256((size_t)P * inter * 2);
   w.o = reinterpret_cast<float*>(p);
+  (void)hidden;
   return w;
 }
 
@@ -180,93 +186,84 @@ moe_route(const float* __restrict__ logits, const float* __restrict__ bias, int 
   }
 }
 
-// Pairs routed to expert e, in pair order, into LDS; returns their count.
-__device__ int gather_pairs(const int32_t* __restrict__ ids, int P, int e, int* plist) {
-  __shared__ int cnt_sh;
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    int cnt = 0;
-    for (int base = 0; base < P; base += 64) {
-      const int p = base + lane;
-      const bool hit = (p < P) && ids[p] == e;
-      const uint64_t m = __ballot(hit);
-      if (hit) plist[cnt + __popcll(m & ((1ull << lane) - 1ull))] = p;
-      cnt += __popcll(m);
-    }
-    if (lane == 0) cnt_sh = cnt;
-  }
-  __syncthreads();
-  return cnt_sh;
-}
+// Pairs routed to expert e, in pair order, written to lists + e*T (pair
+// index) and tlists + e*T (its token); counts[e] = their number.  One
+// workgroup per expert: every wave scans a contiguous share of the routing
+// table (ids loaded in one round), a prefix over the waves orders the
+// shares, a second ballot pass writes the lists.  An expert appears at most
+// once per token, so T entries always suffice.
+constexpr int kListThreads = 256;
+constexpr int kListRegs = 16;   // routing-table chunks of 64 held per wave
 
-// Pairs routed to expert e, in pair order: plist[i] = pair index, tlist[i] =
-// its token (pair / top_k).  Every wave scans a contiguous share of the
-// routing table (its ids are loaded in one round), a prefix over the waves
-// orders the shares, a second ballot pass writes the lists.
-constexpr int kGatherRegs = 8;   // routing-table chunks of 64 held per wave per round
-
-__device__ int gather_pairs_all(const int32_t* __restrict__ ids, int P, int top_k, int e,
-                                int* plist, int* tlist) {
-  __shared__ int wcnt[16];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+__global__ void __launch_bounds__(kListThreads)
+moe_lists(const int32_t* __restrict__ ids, int P, int T, int top_k, int32_t* __restrict__ plists,
+          int32_t* __restrict__ tlists, int32_t* __restrict__ counts) {
+  __shared__ int wcnt[kListThreads / 64];
+  const int e = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = kListThreads / 64;
   const int nchunks = (P + 63) / 64;
   const int per = (nchunks + nw - 1) / nw;
   const int c0 = wave * per, c1 = (c0 + per < nchunks) ? c0 + per : nchunks;
-  uint64_t masks[kGatherRegs];
+  int32_t* pl = plists + (int64_t)e * T;
+  int32_t* tl = tlists + (int64_t)e * T;
+  const uint64_t lt = (1ull << lane) - 1ull;
   int cnt = 0;
-  const bool inreg = (c1 - c0) <= kGatherRegs;
-  if (inreg) {
-    int v[kGatherRegs];
+  if (c1 - c0 <= kListRegs) {
+    uint64_t masks[kListRegs];
+    int v[kListRegs];
 #pragma unroll
-    for (int i = 0; i < kGatherRegs; ++i) {
+    for (int i = 0; i < kListRegs; ++i) {
       const int p = (c0 + i) * 64 + lane;
       v[i] = (c0 + i < c1 && p < P) ? ids[p] : -1;
     }
 #pragma unroll
-    for (int i = 0; i < kGatherRegs; ++i) {
+    for (int i = 0; i < kListRegs; ++i) {
       masks[i] = __ballot(v[i] == e);
       cnt += __popcll(masks[i]);
     }
+    if (lane == 0) wcnt[wave] = cnt;
+    __syncthreads();
+    int base = 0, total = 0;
+    for (int i = 0; i < nw; ++i) {
+      if (i < wave) base += wcnt[i];
+      total += wcnt[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kListRegs; ++i) {
+      const int p = (c0 + i) * 64 + lane;
+      if ((masks[i] >> lane) & 1ull) {
+        const int slot = base + __popcll(masks[i] & lt);
+        pl[slot] = p;
+        tl[slot] = p / top_k;
+      }
+      base += __popcll(masks[i]);
+    }
+    if (threadIdx.x == 0) counts[e] = total;
   } else {
     for (int c = c0; c < c1; ++c) {
       const int p = c * 64 + lane;
       cnt += __popcll(__ballot((p < P) && ids[p] == e));
     }
-  }
-  if (lane == 0) wcnt[wave] = cnt;
-  __syncthreads();
-  int base = 0, total = 0;
-  for (int i = 0; i < nw; ++i) {
-    if (i < wave) base += wcnt[i];
-    total += wcnt[i];
-  }
-  const uint64_t lt = (1ull << lane) - 1ull;
-  if (inreg) {
-#pragma unroll
-    for (int i = 0; i < kGatherRegs; ++i) {
-      const int p = (c0 + i) * 64 + lane;
-      if ((masks[i] >> lane) & 1ull) {
-        const int slot = base + __popcll(masks[i] & lt);
-        plist[slot] = p;
-        tlist[slot] = p / top_k;
-      }
-      base += __popcll(masks[i]);
+    if (lane == 0) wcnt[wave] = cnt;
+    __syncthreads();
+    int base = 0, total = 0;
+    for (int i = 0; i < nw; ++i) {
+      if (i < wave) base += wcnt[i];
+      total += wcnt[i];
     }
-  } else {
     for (int c = c0; c < c1; ++c) {
       const int p = c * 64 + lane;
       const bool hit = (p < P) && ids[p] == e;
       const uint64_t m = __ballot(hit);
       if (hit) {
         const int slot = base + __popcll(m & lt);
-        plist[slot] = p;
-        tlist[slot] = p / top_k;
+        pl[slot] = p;
+        tl[slot] = p / top_k;
       }
       base += __popcll(m);
     }
+    if (threadIdx.x == 0) counts[e] = total;
   }
-  __syncthreads();
-  return total;
 }
 
 __device__ __forceinline__ v8h dequant8_w(uint32_t codes, _Float16 s16) {
@@ -281,317 +278,322 @@ __device__ __forceinline__ v8h dequant8_w(uint32_t codes, _Float16 s16) {
   return r;
 }
 
-// FC = 1: act = x fp16 [T, K] (row = pair / top_k); out = h fp32 [P, N] + pmax.
-// FC = 2: act = h fp32 [P, K] scaled by 2^-e(pmax[p]); out = o fp32 [P, N].
-template <int FC>
-__global__ void __launch_bounds__(kFcThreads)
-moe_fc(const void* __restrict__ act, const int32_t* __restrict__ ids, int P, int top_k,
-       uint32_t* __restrict__ pmax, const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_sf,
-       const float* __restrict__ w_g, int N, int K, float* __restrict__ out) {
-  extern __shared__ int plist[];
-  const int e = blockIdx.y;
-  const int cnt = gather_pairs(ids, P, e, plist);
-  if (cnt == 0) return;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int l32 = lane & 31, h = lane >> 5;
-  const int n0 = blockIdx.x * kFcRows + wv * 32;
-  const int nrow = n0 + l32;
-  const bool nvalid = nrow < N;
-  const int64_t kb2 = K / 2, kb16 = K / 16;
-  const uint8_t* wr = w + ((int64_t)e * N + (nvalid ? nrow : 0)) * kb2;
-  const uint8_t* sr = w_sf + ((int64_t)e * N + (nvalid ? nrow : 0)) * kb16;
-  const float ge = w_g[e];
-  const v8h zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+// Expert FFN layer.  A unit of work is (expert e, tile of 256 weight rows,
+// pass of up to 160 of the expert's tokens); an expert with more tokens is
+// cut into balanced passes.  Workgroup (x, e, z) takes passes z, z +
+// gridDim.z, ... and, within each pass, R consecutive row tiles streamed back
+// to back (R > 1 when experts x tiles exceeds the compute units, so that the
+// units split evenly over them).  8 waves x one 32-row
+// v_mfma_f32_32x32x16_f16 tile, five 32-token tiles.  K goes in 128-k
+// chunks; lane (row r, half h) owns the 64 k at 64 h of a chunk: two 16-byte
+// code loads and one 4-byte load of its four E4M3 bytes, issued three chunks
+// ahead (across row tiles) into registers and used as loaded (no widening or
+// packing that would make the compiler wait for them early).  MFMA m of a
+// chunk takes k = 64 h + 8 m .. + 7 from both operands.  The FP16 activations
+// of a chunk are loaded two chunks ahead into registers and written to LDS
+// one chunk ahead.  Loads are issued in the order they are needed and the
+// chunk barrier waits for LDS traffic only, so each wait covers just what the
+// next step uses.  Requires K % 64 == 0.
+// FC = 1: act = x [T, K] (row = token).  out = h [P, N] FP16 with, per pair
+//         and row tile, h scaled by 2^-et (et = exponent of the tile's
+//         largest h, stored in etile [P, nt1]); pmax[p] = largest h (fp32
+//         bits, integer max: order independent).
+// FC = 2: act = h [P, K]; staging rescales each 256-k tile by 2^(et - e),
+//         e = exponent of pmax[p], so the pair's values share one scale and
+//         none can overflow FP16.  out = o [P, N] fp32 = h . W^T * g * 2^e.
+constexpr int kFwThreads = 512;
+constexpr int kFwRows = 256;              // weight rows per tile
+constexpr int kFwKC = 128;                // k per chunk
+constexpr int kFwTT = 5;                  // 32-token MFMA tiles per pass
+constexpr int kFwTok = 32 * kFwTT;        // tokens per pass at most
+constexpr int kFwPitch = kFwKC + 8;       // halves per staged token row (+16 B skew)
+constexpr int kFwVec = kFwTok * kFwKC / 8 / kFwThreads;   // staged 8-element vectors per thread
+constexpr int kFwWBuf = 4;                // weight register buffers (loads three chunks ahead)
+constexpr int kFwMaxZ = 1024;             // grid z (more passes handled in a loop)
+constexpr int kFwMaxT1 = 32;              // fc1 row tiles (inter <= 8192)
 
-  for (int t0 = 0; t0 < cnt; t0 += 32 * kTokTiles) {
-    // this lane's token slot in each tile, its activation row and scale
-    const void* arow[kTokTiles];
-    float ainv[kTokTiles];
-    bool avalid[kTokTiles];
+// Workgroup barrier that waits only for this wave's LDS operations.
+// __syncthreads() also waits for every outstanding global load, which would
+// drain the weight loads issued chunks ahead at every chunk.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int V> struct IntC { static constexpr int value = V; };
+
+struct WChunk {
+  uint4 q0, q1;     // 64 codes
+  uint32_t sc;      // their four E4M3 block scales
+};
+
+
+__device__ __forceinline__ int exponent_of(uint32_t bits) {
+  return bits == 0u ? 0 : (int)((bits >> 23) & 0xFFu) - 127;
+}
+
+template <int FC>
+__global__ void __launch_bounds__(kFwThreads)
+moe_fc_wide(const _Float16* __restrict__ act, const int32_t* __restrict__ plists,
+            const int32_t* __restrict__ tlists, const int32_t* __restrict__ counts, int T,
+            uint32_t* __restrict__ pmax, int32_t* __restrict__ etile, int nt1,
+            const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_sf,
+            const float* __restrict__ w_g, int N, int K, int R, void* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) _Float16 xs[2][kFwTok * kFwPitch];
+  __shared__ int spair[kFwTok];   // pair of each token slot of the pass
+  __shared__ int srow[kFwTok];    // its activation row
+  __shared__ int sexp[kFwTok];    // fc2: exponent e of the pair's largest h
+  __shared__ float redmax[FC == 1 ? kFwThreads / 64 : 1][kFwTok];   // fc1: per-wave largest h
+  // fc2: factor 2^(et - e) of each fc1 row tile t of each slot's pair
+  __shared__ _Float16 sfac[FC == 2 ? kFwMaxT1 : 1][kFwTok];
+  const int e = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int32_t* pl = plists + (int64_t)e * T;
+  const int32_t* tl = tlists + (int64_t)e * T;
+  // the first pass starts at the list head: load it together with the count
+  int lp = 0, lt = 0;
+  if (blockIdx.z == 0 && tid < kFwTok) {
+    const int idx = tid < T ? tid : T - 1;
+    lp = pl[idx];
+    if (FC == 1) lt = tl[idx];
+  }
+  const int cnt = counts[e];
+  const int np = (cnt + kFwTok - 1) / kFwTok;   // passes
+  if ((int)blockIdx.z >= np) return;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r32 = lane & 31, h = lane >> 5;
+  const int nch = (K + kFwKC - 1) / kFwKC;
+  const int nchp = (nch + kFwWBuf - 1) / kFwWBuf * kFwWBuf;   // whole rounds of four (extra chunks are zero)
+  const int tiles = (N + kFwRows - 1) / kFwRows;
+  const int xt0 = blockIdx.x * R;
+  const int ntile = (tiles - xt0 < R) ? tiles - xt0 : R;
+  const float ge = w_g[e];
+  const uint8_t* we = w + (int64_t)e * N * (K / 2);
+  const uint8_t* se = w_sf + (int64_t)e * N * (K / 16);
+
+  // this lane's weight row in row tile ti (rows past N re-read row N-1;
+  // they are not stored)
+  auto wrow = [&](int ti, const uint8_t*& wr, const uint8_t*& sr) __attribute__((always_inline)) {
+    int n = (xt0 + ti) * kFwRows + wave * 32 + r32;
+    n = n < N ? n : N - 1;
+    wr = we + (int64_t)n * (K / 2);
+    sr = se + (int64_t)n * (K / 16);
+  };
+  WChunk wb[kFwWBuf];
+  // chunk c of a row (chunks past K re-read k = 0; compute() zeroes them)
+  auto load_w = [&](const uint8_t* wr, const uint8_t* sr, int c, WChunk& d) __attribute__((always_inline)) {
+    int k = c * kFwKC + 64 * h;
+    k = k < K ? k : 0;
+    d.q0 = *reinterpret_cast<const uint4*>(wr + k / 2);
+    d.q1 = *reinterpret_cast<const uint4*>(wr + k / 2 + 16);
+    d.sc = *reinterpret_cast<const uint32_t*>(sr + k / 16);
+  };
+
+  // staging: vector i of a thread = token slot (tid + 512 i) / 16 = 32 i +
+  // tid / 16 (token tile i), 8 k at 8 (tid % 16); only the pass's token
+  // tiles are staged
+  v8h stg[2][kFwVec];
+  const int kq = tid % (kFwKC / 8);
+  int64_t abase[kFwVec];     // element offset of the slot's activation row
+  bool sval[kFwVec];
+  auto stage_load = [&](int c, v8h (&dst)[kFwVec], int ntt) __attribute__((always_inline)) {
+    const int k0 = c * kFwKC + 8 * kq;
+    const int k = k0 < K ? k0 : 8 * kq;
 #pragma unroll
-    for (int tt = 0; tt < kTokTiles; ++tt) {
-      const int slot = t0 + tt * 32 + l32;
-      avalid[tt] = slot < cnt;
-      const int p = avalid[tt] ? plist[slot] : 0;
-      if constexpr (FC == 1) {
-        arow[tt] = reinterpret_cast<const _Float16*>(act) + (int64_t)(p / top_k) * K;
-        ainv[tt] = 1.0f;
-      } else {
-        arow[tt] = reinterpret_cast<const float*>(act) + (int64_t)p * K;
-        const uint32_t mb = pmax[p];
-        const int ex = (mb == 0u) ? 0 : (int)((mb >> 23) & 0xFFu) - 127;
-        ainv[tt] = __builtin_ldexpf(1.0f, -ex);
+    for (int i = 0; i < kFwVec; ++i)
+      if (i < ntt) dst[i] = *reinterpret_cast<const v8h*>(act + abase[i] + k);
+  };
+  auto stage_store = [&](int c, const v8h (&src)[kFwVec], _Float16* xb, int ntt) __attribute__((always_inline)) {
+    const bool kv = c * kFwKC + 8 * kq < K;
+    const int t = (c >> 1) < nt1 ? (c >> 1) : nt1 - 1;   // fc2: fc1 row tile of the chunk
+#pragma unroll
+    for (int i = 0; i < kFwVec; ++i) {
+      if (i < ntt) {
+        v8h val = src[i];
+        if constexpr (FC == 2) {
+          const _Float16 f = sfac[t][32 * i + tid / 16];
+          const v2h f2 = {f, f};
+          v2h* pv = reinterpret_cast<v2h*>(&val);
+          pv[0] = pv[0] * f2; pv[1] = pv[1] * f2; pv[2] = pv[2] * f2; pv[3] = pv[3] * f2;
+        }
+        if (!(kv && sval[i])) val = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+        *reinterpret_cast<v8h*>(xb + (32 * i + tid / 16) * kFwPitch + 8 * kq) = val;
       }
     }
-    const int ntiles = (cnt - t0 + 31) / 32;
-    v16f acc[kTokTiles];
+  };
+
+  v16f acc[kFwTT];
+  auto compute = [&](int c, const _Float16* xb, const WChunk& d, int ntt) __attribute__((always_inline)) {
+    const bool kv = c * kFwKC + 64 * h < K;
+    const uint32_t words[8] = {d.q0.x, d.q0.y, d.q0.z, d.q0.w, d.q1.x, d.q1.y, d.q1.z, d.q1.w};
+    _Float16 s16[4];
+    s16[0] = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)d.sc, 0);
+    s16[1] = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)d.sc, 1);
+    s16[2] = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)d.sc, 2);
+    s16[3] = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)d.sc, 3);
 #pragma unroll
-    for (int tt = 0; tt < kTokTiles; ++tt)
+    for (int m = 0; m < 8; ++m) {
+      const v8h af = dequant8_w(kv ? words[m] : 0u, s16[m >> 1]);
+#pragma unroll
+      for (int tt = 0; tt < kFwTT; ++tt) {
+        if (tt >= ntt) break;   // wave-uniform
+        const v8h bf = *reinterpret_cast<const v8h*>(xb + (32 * tt + r32) * kFwPitch + 64 * h + 8 * m);
+        acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf, acc[tt], 0, 0, 0);
+      }
+    }
+  };
+
+  // results of row tile ti: acc[tt][r] = weight row n0 + 8 (r / 4) + 4 h +
+  // r % 4, token slot 32 tt + r32
+  auto epilogue = [&](int ti, int ntok, int ntt) __attribute__((always_inline)) {
+    const int xt = xt0 + ti;
+    const int n0 = xt * kFwRows + wave * 32;
+    if constexpr (FC == 1) {
+#pragma unroll
+      for (int tt = 0; tt < kFwTT; ++tt) {
+        if (tt >= ntt) break;
+        float m = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m = __builtin_fmaxf(m, relu2_f32(acc[tt][r] * ge));
+        if (n0 >= N) m = 0.0f;
+        m = __builtin_fmaxf(m, __shfl_xor(m, 32, 64));
+        if (h == 0) redmax[wave][32 * tt + r32] = m;
+      }
+      lds_barrier();
+#pragma unroll
+      for (int tt = 0; tt < kFwTT; ++tt) {
+        if (tt >= ntt) break;
+        const int slot = 32 * tt + r32;
+        float tmax = redmax[0][slot];
+#pragma unroll
+        for (int wv = 1; wv < kFwThreads / 64; ++wv) tmax = __builtin_fmaxf(tmax, redmax[wv][slot]);
+        const int ex = exponent_of(__float_as_uint(tmax));
+        const float sc = __builtin_ldexpf(1.0f, -ex);
+        const bool sv = slot < ntok;
+        const int p = spair[slot];
+        if (sv && n0 < N) {
+          _Float16* hp = reinterpret_cast<_Float16*>(out) + (int64_t)p * N + n0 + 4 * h;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v4h o4;
+            o4[0] = (_Float16)(relu2_f32(acc[tt][4 * q + 0] * ge) * sc);
+            o4[1] = (_Float16)(relu2_f32(acc[tt][4 * q + 1] * ge) * sc);
+            o4[2] = (_Float16)(relu2_f32(acc[tt][4 * q + 2] * ge) * sc);
+            o4[3] = (_Float16)(relu2_f32(acc[tt][4 * q + 3] * ge) * sc);
+            *reinterpret_cast<v4h*>(hp + 8 * q) = o4;
+          }
+        }
+        if (sv && wave == 0 && h == 0) {
+          etile[(int64_t)p * nt1 + xt] = ex;
+          atomicMax(pmax + p, __float_as_uint(tmax));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < kFwTT; ++tt) {
+        if (tt >= ntt) break;
+        const int slot = 32 * tt + r32;
+        const float scale = __builtin_ldexpf(ge, sexp[slot]);
+        if (slot < ntok && n0 < N) {
+          float* op = reinterpret_cast<float*>(out) + (int64_t)spair[slot] * N + n0 + 4 * h;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float4 v;
+            v.x = acc[tt][4 * q + 0] * scale;
+            v.y = acc[tt][4 * q + 1] * scale;
+            v.z = acc[tt][4 * q + 2] * scale;
+            v.w = acc[tt][4 * q + 3] * scale;
+            *reinterpret_cast<float4*>(op + 8 * q) = v;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < kFwTT; ++tt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[tt][r] = 0.0f;
-
-    for (int k0 = 0; k0 < K; k0 += 64) {
-      const int k = k0 + 32 * h;
-      const bool kv = k < K;
-      const uint4 wc = (nvalid && kv) ? *reinterpret_cast<const uint4*>(wr + k / 2) : make_uint4(0, 0, 0, 0);
-      const uint32_t sw = (nvalid && kv) ? (uint32_t)*reinterpret_cast<const uint16_t*>(sr + k / 16) : 0u;
-      const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)sw, 0);
-      const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)sw, 1);
-      v8h wf[4];
-      wf[0] = dequant8_w(wc.x, s0);
-      wf[1] = dequant8_w(wc.y, s0);
-      wf[2] = dequant8_w(wc.z, s1);
-      wf[3] = dequant8_w(wc.w, s1);
-#pragma unroll
-      for (int tt = 0; tt < kTokTiles; ++tt) {
-        if (tt >= ntiles) break;
-        const bool v = avalid[tt] && kv;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          v8h af;
-          if constexpr (FC == 1) {
-            af = v ? *reinterpret_cast<const v8h*>(reinterpret_cast<const _Float16*>(arow[tt]) + k + 8 * m)
-                   : zero8;
-          } else {
-            if (v) {
-              const float* src = reinterpret_cast<const float*>(arow[tt]) + k + 8 * m;
-              const float4 lo = *reinterpret_cast<const float4*>(src);
-              const float4 hi = *reinterpret_cast<const float4*>(src + 4);
-              const float sc = ainv[tt];
-              af[0] = (_Float16)(lo.x * sc); af[1] = (_Float16)(lo.y * sc);
-              af[2] = (_Float16)(lo.z * sc); af[3] = (_Float16)(lo.w * sc);
-              af[4] = (_Float16)(hi.x * sc); af[5] = (_Float16)(hi.y * sc);
-              af[6] = (_Float16)(hi.z * sc); af[7] = (_Float16)(hi.w * sc);
-            } else {
-              af = zero8;
-            }
-          }
-          // weights are the A operand (rows = weight rows), tokens the B operand
-          acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[m], af, acc[tt], 0, 0, 0);
-        }
-      }
-    }
-
-    // epilogue: D[i][j] -> weight row n0 + i, token slot t0 + tt*32 + j
-#pragma unroll
-    for (int tt = 0; tt < kTokTiles; ++tt) {
-      if (tt >= ntiles) break;
-      const int slot = t0 + tt * 32 + l32;
-      const bool sv = slot < cnt;
-      const int p = sv ? plist[slot] : 0;
-      float vmax = 0.0f;
-      float scale = ge;
-      if constexpr (FC == 2) scale = ge / ainv[tt];   // ge * 2^e, exact power-of-two scaling
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = (r >> 2) * 8 + h * 4 + (r & 3);
-        const int n = n0 + i;
-        float v = acc[tt][r] * scale;
-        if constexpr (FC == 1) {
-          v = relu2_f32(v);
-          vmax = __builtin_fmaxf(vmax, v);
-        }
-        if (sv && n < N) out[(int64_t)p * N + n] = v;
-      }
-      if constexpr (FC == 1) {
-        vmax = __builtin_fmaxf(vmax, __shfl_xor(vmax, 32, 64));
-        if (sv && h == 0) atomicMax(pmax + p, __float_as_uint(vmax));
-      }
-    }
-  }
-}
-
-// Streaming version of fc1/fc2 (the one launched).  One workgroup = 4 waves
-// = 64 weight rows of one expert, each wave 16 rows over the whole K (two
-// workgroups fit a CU, so one computes while the other waits on memory).
-// Each lane issues all of its weight-code loads (32 codes + 2 E4M3 bytes per
-// 128-k chunk, up to 2048 k) before any arithmetic.  The expert's token rows
-// are staged in LDS as FP16 in 256-k chunks (fc2 applies the per-pair power
-// of two while staging), double-buffered, and feed v_mfma_f32_16x16x32_f16 as
-// the second operand, 64 tokens per pass.
-constexpr int kMsThreads = 256;
-constexpr int kMsRows = 64;
-constexpr int kMsKC = 256;               // staged k per LDS chunk
-constexpr int kMsTok = 64;               // tokens per pass (4 tiles of 16)
-constexpr int kMsSB = 2048;              // k per register superblock (16 chunks of 128)
-constexpr int kMsPitch = kMsKC + 8;      // halves per staged token row (+16 B skew)
-
-size_t moe_stream_lds(int tokens) {
-  return 2 * align256((size_t)tokens * 4) + 2 * (size_t)kMsTok * kMsPitch * 2;
-}
-
-template <int FC>
-__global__ void __launch_bounds__(kMsThreads)
-moe_fc_stream(const void* __restrict__ act, const int32_t* __restrict__ ids, int P, int top_k,
-              uint32_t* __restrict__ pmax, const uint8_t* __restrict__ w,
-              const uint8_t* __restrict__ w_sf, const float* __restrict__ w_g, int N, int K,
-              float* __restrict__ out, int tok_off) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
-  int* plist = reinterpret_cast<int*>(sm);
-  int* tlist = reinterpret_cast<int*>(sm + tok_off / 2);
-  _Float16* xsb[2] = {reinterpret_cast<_Float16*>(sm + tok_off),
-                      reinterpret_cast<_Float16*>(sm + tok_off + kMsTok * kMsPitch * 2)};
-  const int e = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r16 = lane & 15, g = lane >> 4;
-  const int nbase = blockIdx.x * kMsRows + wave * 16;
-  const int nrow = nbase + r16;
-  const bool nvalid = nrow < N;
-  const int64_t kb2 = K / 2, kb16 = K / 16;
-  const uint8_t* wr = w + ((int64_t)e * N + (nvalid ? nrow : 0)) * kb2;
-  const uint8_t* sr = w_sf + ((int64_t)e * N + (nvalid ? nrow : 0)) * kb16;
-  const v8h zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-  constexpr int kStageVec = (kMsTok * kMsKC / 8) / kMsThreads;   // 8-element vectors per thread
-
-  const int cnt = gather_pairs_all(ids, P, top_k, e, plist, tlist);
-  if (cnt == 0) return;
-  const float ge = w_g[e];
-
-  uint4 wc[16];
-  uint32_t ws[16];
-  auto load_w = [&](int kb) {
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const int k = kb + 128 * c + 32 * g;
-      const bool v = nvalid && k < K;
-      wc[c] = v ? *reinterpret_cast<const uint4*>(wr + k / 2) : make_uint4(0, 0, 0, 0);
-      ws[c] = v ? (uint32_t)*reinterpret_cast<const uint16_t*>(sr + k / 16) : 0u;
-    }
   };
 
-  // staging of token rows: global -> registers -> LDS (FP16)
-  v8h stg[kStageVec];
-  auto stage_load = [&](int t0, int kc) {
 #pragma unroll
-    for (int i = 0; i < kStageVec; ++i) {
-      const int v = tid + kMsThreads * i;
-      const int slot = v / (kMsKC / 8), kq = v % (kMsKC / 8);
-      const int k = kc + 8 * kq;
-      v8h val = zero8;
-      if (t0 + slot < cnt && k < K) {
-        if constexpr (FC == 1) {
-          val = *reinterpret_cast<const v8h*>(reinterpret_cast<const _Float16*>(act) +
-                                              (int64_t)tlist[t0 + slot] * K + k);
-        } else {
-          const int p = plist[t0 + slot];
-          const uint32_t mb = pmax[p];
-          const int ex = (mb == 0u) ? 0 : (int)((mb >> 23) & 0xFFu) - 127;
-          const float sc = __builtin_ldexpf(1.0f, -ex);
-          const float* src = reinterpret_cast<const float*>(act) + (int64_t)p * K + k;
-          const float4 lo = *reinterpret_cast<const float4*>(src);
-          const float4 hi = *reinterpret_cast<const float4*>(src + 4);
-          val[0] = (_Float16)(lo.x * sc); val[1] = (_Float16)(lo.y * sc);
-          val[2] = (_Float16)(lo.z * sc); val[3] = (_Float16)(lo.w * sc);
-          val[4] = (_Float16)(hi.x * sc); val[5] = (_Float16)(hi.y * sc);
-          val[6] = (_Float16)(hi.z * sc); val[7] = (_Float16)(hi.w * sc);
-        }
-      }
-      stg[i] = val;
+  for (int tt = 0; tt < kFwTT; ++tt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[tt][r] = 0.0f;
+  for (int z = blockIdx.z; z < np; z += gridDim.z) {
+    // balanced passes: the first cnt % np passes take one token more
+    const int base = cnt / np, rem = cnt % np;
+    const int ntok = base + (z < rem ? 1 : 0);
+    const int t0 = z * base + (z < rem ? z : rem);
+    const int ntt = (ntok + 31) / 32;
+    if (z != (int)blockIdx.z) __syncthreads();   // a previous pass is done with the LDS buffers
+    if (t0 != 0 && tid < kFwTok) {
+      lp = pl[t0 + (tid < ntok ? tid : 0)];
+      if (FC == 1) lt = tl[t0 + (tid < ntok ? tid : 0)];
     }
-  };
-  auto stage_store = [&](_Float16* xs) {
-#pragma unroll
-    for (int i = 0; i < kStageVec; ++i) {
-      const int v = tid + kMsThreads * i;
-      const int slot = v / (kMsKC / 8), kq = v % (kMsKC / 8);
-      *reinterpret_cast<v8h*>(xs + slot * kMsPitch + 8 * kq) = stg[i];
+    // slots past the pass use token 0 / pair 0 (computed, never stored)
+    if (tid < kFwTok) {
+      const int p = tid < ntok ? lp : 0;
+      spair[tid] = p;
+      srow[tid] = FC == 1 ? (tid < ntok ? lt : 0) : p;
     }
-  };
-
-  // one superblock of up to 2048 k for tokens [t0, t0+64)
-  auto superblock = [&](int t0, int kb, v4f* acc) {
-    stage_store(xsb[0]);
-    __syncthreads();
+    // weights of chunks 0..2, then (fc2) the pairs' maxima and the
+    // activations of chunks 0 and 1, all in flight together
+    const uint8_t *wr, *sr;
+    wrow(0, wr, sr);
+    load_w(wr, sr, 0, wb[0]);
+    load_w(wr, sr, 1, wb[1]);
+    load_w(wr, sr, 2, wb[2]);
+    lds_barrier();
 #pragma unroll
-    for (int q = 0; q < kMsSB / kMsKC; ++q) {
-      const int kc = kb + q * kMsKC;
-      if (kc >= K) break;
-      const bool more = (q + 1 < kMsSB / kMsKC) && (kc + kMsKC < K);
-      if (more) stage_load(t0, kc + kMsKC);        // next chunk's loads in flight
-      const _Float16* xs = xsb[q & 1];
-#pragma unroll
-      for (int c2 = 0; c2 < kMsKC / 128; ++c2) {
-        const int c = q * (kMsKC / 128) + c2;     // chunk within the superblock
-        const int k = kc + 128 * c2 + 32 * g;
-        if (kc + 128 * c2 >= K) break;
-        const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)ws[c], 0);
-        const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)ws[c], 1);
-        v8h af[4];
-        af[0] = dequant8_w(wc[c].x, s0);
-        af[1] = dequant8_w(wc[c].y, s0);
-        af[2] = dequant8_w(wc[c].z, s1);
-        af[3] = dequant8_w(wc[c].w, s1);
-        const bool kv = k < K;
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          if (t0 + 16 * tt >= cnt) break;
-          const _Float16* xrow = xs + (16 * tt + r16) * kMsPitch + 128 * c2 + 32 * g;
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const v8h bf = kv ? *reinterpret_cast<const v8h*>(xrow + 8 * m) : zero8;
-            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[m], bf, acc[tt], 0, 0, 0);
-          }
-        }
-      }
-      if (more) stage_store(xsb[(q + 1) & 1]);
-      __syncthreads();
+    for (int i = 0; i < kFwVec; ++i) {
+      const int slot = 32 * i + tid / 16;
+      sval[i] = slot < ntok;
+      abase[i] = (int64_t)srow[slot] * K;
     }
-  };
-
-  auto epilogue = [&](int t0, const v4f* acc) {
-    // D[i][j] -> weight row nbase + 4g + r, token slot t0 + 16tt + (lane & 15)
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      if (t0 + 16 * tt >= cnt) break;
-      const int slot = t0 + 16 * tt + r16;
-      const bool sv = slot < cnt;
-      const int p = sv ? plist[slot] : 0;
-      float scale = ge;
-      if constexpr (FC == 2) {
-        const uint32_t mb = pmax[p];
-        const int ex = (mb == 0u) ? 0 : (int)((mb >> 23) & 0xFFu) - 127;
-        scale = __builtin_ldexpf(ge, ex);
+    stage_load(0, stg[0], ntt);
+    stage_load(1, stg[1], ntt);
+    if constexpr (FC == 2) {
+      // each slot's exponent e and the factors of its fc1 row tiles
+      // (d = et - e <= 0; d > 0 only for an all-zero tile; factors below
+      // FP16's range are 0)
+      for (int idx = tid; idx < kFwTok * nt1; idx += kFwThreads) {
+        const int t = idx / kFwTok, slot = idx - t * kFwTok;
+        const int p = spair[slot];
+        const int ex = exponent_of(pmax[p]);
+        int d = etile[(int64_t)p * nt1 + t] - ex;
+        d = d > 0 ? 0 : d;
+        sfac[t][slot] = d < -24 ? (_Float16)0.0f : (_Float16)__builtin_ldexpf(1.0f, d);
+        if (t == 0) sexp[slot] = ex;
       }
-      float vmax = 0.0f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int n = nbase + 4 * g + r;
-        float v = acc[tt][r] * scale;
-        if constexpr (FC == 1) {
-          v = relu2_f32(v);
-          vmax = __builtin_fmaxf(vmax, v);
-        }
-        if (sv && n < N) out[(int64_t)p * N + n] = v;
-      }
-      if constexpr (FC == 1) {
-        vmax = __builtin_fmaxf(vmax, __shfl_xor(vmax, 16, 64));
-        vmax = __builtin_fmaxf(vmax, __shfl_xor(vmax, 32, 64));
-        if (sv && g == 0) atomicMax(pmax + p, __float_as_uint(vmax));
-      }
+      lds_barrier();
     }
-  };
-
-  if (cnt <= kMsTok && K <= kMsSB) {
-    // common case: one pass, one superblock, straight-line
-    load_w(0);
-    stage_load(0, 0);
-    v4f acc[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) acc[tt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    superblock(0, 0, acc);
-    epilogue(0, acc);
-    return;
-  }
-  for (int t0 = 0; t0 < cnt; t0 += kMsTok) {
-    v4f acc[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) acc[tt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int kb = 0; kb < K; kb += kMsSB) {
-      load_w(kb);
-      stage_load(t0, kb);
-      superblock(t0, kb, acc);
+    stage_store(0, stg[0], xs[0], ntt);
+    lds_barrier();
+    // chunk c of a tile uses weight buffer c % 4, staging registers and LDS
+    // buffer c % 2 (nchp is a multiple of four, so this holds across tiles).
+    // Step c loads the activations of chunk c + 2 and the weights of chunk
+    // c + 3, past the tile's end those of the next tile (of this one past
+    // the last: re-read, unused).
+    for (int ti = 0; ti < ntile; ++ti) {
+      const uint8_t *wn, *sn;
+      wrow(ti + 1 < ntile ? ti + 1 : ti, wn, sn);
+      auto step = [&](int c, auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
+        stage_load(c + 2 < nchp ? c + 2 : c + 2 - nchp, stg[j & 1], ntt);
+        const bool nx = c + 3 >= nchp;
+        load_w(nx ? wn : wr, nx ? sn : sr, nx ? c + 3 - nchp : c + 3, wb[(j + 3) % kFwWBuf]);
+        compute(c, xs[j & 1], wb[j], ntt);
+        stage_store(c + 1 < nchp ? c + 1 : 0, stg[(j + 1) & 1], xs[(j + 1) & 1], ntt);
+        lds_barrier();
+      };
+      for (int c = 0; c < nchp; c += kFwWBuf) {
+        step(c, IntC<0>{});
+        step(c + 1, IntC<1>{});
+        step(c + 2, IntC<2>{});
+        step(c + 3, IntC<3>{});
+      }
+      epilogue(ti, ntok, ntt);
+      wr = wn;
+      sr = sn;
     }
-    epilogue(t0, acc);
   }
 }
 
@@ -612,50 +614,43 @@ moe_combine4(const float* __restrict__ o, const float* __restrict__ wts, int top
   *reinterpret_cast<v4h*>(out + t * H + n) = r;
 }
 
-__global__ void __launch_bounds__(256)
-moe_combine(const float* __restrict__ o, const float* __restrict__ wts, int top_k, int H,
-            _Float16* __restrict__ out) {
-  const int64_t t = blockIdx.x;
-  for (int n = threadIdx.x; n < H; n += blockDim.x) {
-    float s = 0.0f;
-    for (int j = 0; j < top_k; ++j) s += wts[t * top_k + j] * o[(t * top_k + j) * H + n];
-    out[t * H + n] = (_Float16)s;
-  }
-}
-
 }  // namespace
 
 size_t moe_workspace_bytes(int tokens, int experts, int top_k, int hidden, int inter) {
-  (void)experts;
   const size_t P = (size_t)tokens * top_k;
-  return 3 * align256(P * 4) + align256(P * inter * 4) + align256(P * hidden * 4);
+  const size_t ET = (size_t)experts * tokens;
+  return 3 * align256(P * 4) + align256((size_t)experts * 4) + 2 * align256(ET * 4) +
+         align256(P * fc1_tiles(inter) * 4) + align256(P * inter * 2) + align256(P * hidden * 4);
+}
+
+// Row tiles per workgroup: enough that the (expert, row tile) units of a
+// layer split evenly over the compute units when there are more of them.
+static int tiles_per_wg(int experts, int n, int num_cus) {
+  const int units = experts * ((n + kFwRows - 1) / kFwRows);
+  int r = num_cus > 0 ? units / num_cus : 1;
+  return r < 1 ? 1 : (r > 8 ? 8 : r);
 }
 
 hipError_t launch_moe(const MoeArgs& m, hipStream_t s) {
   const int P = m.tokens * m.top_k;
-  if (m.tokens > 16384) return hipErrorNotSupported;   // the per-expert pair list lives in LDS
-  static std::once_flag once;
-  static hipError_t attr_err = hipSuccess;
-  std::call_once(once, []() {
-    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_fc_stream<1>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 1024);
-    if (attr_err == hipSuccess)
-      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_fc_stream<2>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 1024);
-  });
-  if (attr_err != hipSuccess) return attr_err;
-  MoeWs ws = carve(m.workspace, P, m.hidden, m.inter);
+  MoeWs ws = carve(m.workspace, m.tokens, m.experts, P, m.hidden, m.inter);
+  const int nt1 = fc1_tiles(m.inter);
   hipLaunchKernelGGL(moe_route, dim3((m.tokens + 3) / 4), dim3(256), 0, s, m.logits, m.bias,
                      m.tokens, m.experts, m.top_k, m.n_group, m.topk_group, m.norm, m.scaling,
                      ws.ids, ws.wts, ws.pmax, m.ids_out, m.w_out);
-  const size_t lds = moe_stream_lds(m.tokens);
-  const int tok_off = 2 * (int)align256((size_t)m.tokens * 4);
-  hipLaunchKernelGGL(moe_fc_stream<1>, dim3((m.inter + kMsRows - 1) / kMsRows, m.experts),
-                     dim3(kMsThreads), lds, s, m.x, ws.ids, P, m.top_k, ws.pmax, m.w1, m.w1_sf,
-                     m.w1_g, m.inter, m.hidden, ws.h, tok_off);
-  hipLaunchKernelGGL(moe_fc_stream<2>, dim3((m.hidden + kMsRows - 1) / kMsRows, m.experts),
-                     dim3(kMsThreads), lds, s, ws.h, ws.ids, P, m.top_k, ws.pmax, m.w2, m.w2_sf,
-                     m.w2_g, m.hidden, m.inter, ws.o, tok_off);
+  hipLaunchKernelGGL(moe_lists, dim3(m.experts), dim3(kListThreads), 0, s, ws.ids, P, m.tokens,
+                     m.top_k, ws.plists, ws.tlists, ws.counts);
+  const int zs = (m.tokens + kFwTok - 1) / kFwTok < kFwMaxZ ? (m.tokens + kFwTok - 1) / kFwTok : kFwMaxZ;
+  const int r1 = tiles_per_wg(m.experts, m.inter, m.num_cus);
+  const int r2 = tiles_per_wg(m.experts, m.hidden, m.num_cus);
+  hipLaunchKernelGGL(moe_fc_wide<1>, dim3((nt1 + r1 - 1) / r1, m.experts, zs), dim3(kFwThreads), 0, s,
+                     reinterpret_cast<const _Float16*>(m.x), ws.plists, ws.tlists, ws.counts,
+                     m.tokens, ws.pmax, ws.etile, nt1, m.w1, m.w1_sf, m.w1_g, m.inter, m.hidden, r1,
+                     reinterpret_cast<void*>(ws.h));
+  const int t2 = (m.hidden + kFwRows - 1) / kFwRows;
+  hipLaunchKernelGGL(moe_fc_wide<2>, dim3((t2 + r2 - 1) / r2, m.experts, zs), dim3(kFwThreads), 0, s,
+                     ws.h, ws.plists, ws.tlists, ws.counts, m.tokens, ws.pmax, ws.etile, nt1, m.w2,
+                     m.w2_sf, m.w2_g, m.hidden, m.inter, r2, reinterpret_cast<void*>(ws.o));
   hipLaunchKernelGGL(moe_combine4, dim3(m.tokens, (m.hidden + 1023) / 1024), dim3(256), 0, s, ws.o,
                      ws.wts, m.top_k, m.hidden, reinterpret_cast<_Float16*>(m.out));
   return hipGetLastError();

@@ -26,8 +26,9 @@
 // output is bit-identical to the direct evaluation.
 //
 // Per-group path (per tensor / per expert): a partial-amax kernel writes at
-// most 256 partial maxima per group into the workspace; the row kernel then
-// reduces its group's partials instead of its own row.
+// most 1024 partial maxima per group into the workspace, a second kernel
+// reduces them to one maximum per group, and the row kernel uses that instead
+// of its own row's.
 //
 // A scalar fallback handles inputs that are not 16-byte aligned (or codes not
 // 4-byte aligned) and rows longer than the register cache, with identical
@@ -362,7 +363,9 @@ quant_rows_generic(const uint16_t* __restrict__ x, int64_t k_out, uint8_t* __res
   }
 }
 
-// Partial maxima of |x| over `nparts` slices of each group of elements.
+// Partial maxima of |x| over `nparts` slices of each group of elements.  A
+// slice is read with 16-byte loads (four in flight per lane) when the group
+// and the slice start are 16-byte aligned, element by element otherwise.
 template <int DT>
 __global__ void __launch_bounds__(kMaxThreads)
 group_amax_parts(const uint16_t* __restrict__ x, int64_t group_elems, int64_t chunk, int nparts,
@@ -374,10 +377,45 @@ group_amax_parts(const uint16_t* __restrict__ x, int64_t group_elems, int64_t ch
   const int64_t lo = (int64_t)p * chunk;
   const int64_t hi = (lo + chunk < group_elems) ? lo + chunk : group_elems;
   float m = 0.0f;
-  for (int64_t e = lo + threadIdx.x; e < hi; e += blockDim.x)
-    m = __builtin_fmaxf(m, __builtin_fabsf(unpack1<DT>(base[e])));
+  int64_t e = lo;
+  if (hi > lo && (((uintptr_t)(base + lo)) & 15) == 0) {
+    const u32x4* v = reinterpret_cast<const u32x4*>(base + lo);
+    const int64_t nv = (hi - lo) / 8;
+    for (int64_t i = threadIdx.x; i < nv; i += 4 * kMaxThreads) {
+      u32x4 q[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t j = i + u * kMaxThreads;
+        q[u] = __builtin_nontemporal_load(v + (j < nv ? j : i));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t w4[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          float a, b;
+          unpack2<DT>(w4[t], a, b);
+          m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(a), __builtin_fabsf(b)));
+        }
+      }
+    }
+    e = lo + nv * 8;
+  }
+  for (int64_t i = e + threadIdx.x; i < hi; i += blockDim.x)
+    m = __builtin_fmaxf(m, __builtin_fabsf(unpack1<DT>(base[i])));
   m = block_max(m, red);
   if (threadIdx.x == 0) parts[g * nparts + p] = m;
+}
+
+// Maximum over each group's partial maxima: gmax[g].
+__global__ void __launch_bounds__(kMaxThreads)
+group_amax_final(const float* __restrict__ parts, int nparts, float* __restrict__ gmax) {
+  __shared__ float red[kMaxThreads / 64];
+  const float* pp = parts + (int64_t)blockIdx.x * nparts;
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < nparts; i += blockDim.x) m = __builtin_fmaxf(m, pp[i]);
+  m = block_max(m, red);
+  if (threadIdx.x == 0) gmax[blockIdx.x] = m;
 }
 
 template <int DT, int ACT, int L>
@@ -435,23 +473,31 @@ void launch_rows(const QuantArgs& a, hipStream_t s) {
 }  // namespace
 
 int quant_num_parts(int64_t group_elems) {
-  int64_t p = (group_elems + 4095) / 4096;
-  return (int)(p < 1 ? 1 : (p > 256 ? 256 : p));
+  int64_t p = (group_elems + 16383) / 16384;
+  return (int)(p < 1 ? 1 : (p > 1024 ? 1024 : p));
 }
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
   QuantArgs b = a;
   if (a.group_rows > 1) {
+    // slices of whole 8-element units, so every slice start stays 16-byte
+    // aligned when the group start is
     const int64_t ge = a.group_rows * a.k_out;
-    const int64_t chunk = (ge + a.nparts - 1) / a.nparts;
-    const dim3 grid((unsigned)a.nparts, (unsigned)(a.rows / a.group_rows));
+    const int64_t chunk = ((ge + a.nparts - 1) / a.nparts + 7) / 8 * 8;
+    const int64_t groups = a.rows / a.group_rows;
+    const dim3 grid((unsigned)a.nparts, (unsigned)groups);
     if (a.dtype == kBf16)
       hipLaunchKernelGGL(group_amax_parts<0>, grid, dim3(kMaxThreads), 0, s, (const uint16_t*)a.x,
                          ge, chunk, a.nparts, a.parts);
     else
       hipLaunchKernelGGL(group_amax_parts<1>, grid, dim3(kMaxThreads), 0, s, (const uint16_t*)a.x,
                          ge, chunk, a.nparts, a.parts);
+    float* gmax = a.parts + groups * a.nparts;
+    hipLaunchKernelGGL(group_amax_final, dim3((unsigned)groups), dim3(kMaxThreads), 0, s, a.parts,
+                       a.nparts, gmax);
+    b.parts = gmax;
+    b.nparts = 1;
   } else {
     b.parts = nullptr;
   }

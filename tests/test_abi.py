@@ -80,5 +80,8 @@ def test_moe_validation_without_gpu(nv):
     assert L.nvfp4_moe_w4a16(*args, 4, 10, 2, 64, 64, 3, 1, 1, 1.0, None, 0, None) == nv.NVFP4_EINVAL
     # top_k larger than the kept experts
     assert L.nvfp4_moe_w4a16(*args, 4, 8, 5, 64, 64, 4, 2, 1, 1.0, None, 0, None) == nv.NVFP4_EINVAL
+    # hidden / inter not multiples of 64
+    assert L.nvfp4_moe_w4a16(*args, 4, 8, 2, 96, 64, 4, 2, 1, 1.0, None, 0, None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_moe_w4a16(*args, 4, 8, 2, 64, 32, 4, 2, 1, 1.0, None, 0, None) == nv.NVFP4_EINVAL
     # missing workspace
     assert L.nvfp4_moe_w4a16(*args, 4, 8, 2, 64, 64, 4, 2, 1, 1.0, None, 0, None) == nv.NVFP4_EWORKSPACE
