@@ -6,9 +6,10 @@
 // Five launches, all deterministic (no floating-point atomics):
 //  1. route      : one wave per token.  Lanes hold experts; sigmoid scores
 //                  (the same binary32 exp as the quantizer), biased scores,
-//                  group scores = sum of the group's two best, repeated wave
-//                  argmax for the kept groups and the top-k experts (ties to
-//                  the lower index), weights normalized in rank order.
+//                  group scores = sum of the group's two best; kept groups and
+//                  top-k experts by rank counts in the order "higher score
+//                  first, lower index on ties"; weights normalized in rank
+//                  order.
 //  2. lists      : one workgroup per expert writes the pairs (token, rank)
 //                  routed to it, in pair order, and their count.
 //  3. fc1        : grid (inter/256, experts), 8 waves x 32 weight rows.
@@ -68,23 +69,24 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return (va > vb) || (va == vb && ia < ib);
 }
 
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(v, off, 64);
-    const int oi = __shfl_xor(i, off, 64);
-    if (better(ov, oi, v, i)) { v = ov; i = oi; }
-  }
-}
-
 constexpr int kMaxExpertsPerLane = 4;   // experts <= 256
 
+// One wave per token.  Each selection is made by counting, for every
+// contender, how many others come before it in the (value desc, index asc)
+// order -- the same order as taking repeated maxima with ties to the lower
+// index -- so no serial chain of cross-lane reductions is needed.
 __global__ void __launch_bounds__(256)
 moe_route(const float* __restrict__ logits, const float* __restrict__ bias, int T, int E,
           int top_k, int n_group, int topk_group, int norm, float scaling,
           int32_t* __restrict__ ids, float* __restrict__ wts, uint32_t* __restrict__ pmax,
           int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
-  __shared__ float sb[4][256];
+  __shared__ float sb[4][256];      // biased scores
+  __shared__ float sg[4][256];      // group scores
+  __shared__ int kg[4][256];        // kept-group flags
+  __shared__ float cb[4][256];      // candidates (experts of kept groups): biased score
+  __shared__ int ce[4][256];        // ... and expert index, in expert order
+  __shared__ int sel_e[4][16];      // chosen experts by rank
+  __shared__ float sel_s[4][16];    // their unbiased scores
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t_raw = blockIdx.x * 4 + wv;
   const bool tv = t_raw < T;             // waves past the last token idle but reach the barriers
@@ -98,6 +100,7 @@ moe_route(const float* __restrict__ logits, const float* __restrict__ bias, int 
     if (e < E) {
       s[i] = sigmoid_f32(logits[(int64_t)t * E + e]);
       b[i] = s[i] + bias[e];
+      if (b[i] != b[i]) b[i] = ninf;   // a NaN score ranks below every number
       sb[wv][e] = b[i];
     } else {
       s[i] = 0.0f;
@@ -114,67 +117,63 @@ moe_route(const float* __restrict__ logits, const float* __restrict__ bias, int 
     if (g < n_group) {
       float v1 = ninf, v2 = ninf;
       int i1 = -1, i2 = -1;
+#pragma unroll 8
       for (int e = g * gsize; e < (g + 1) * gsize; ++e) {
         const float v = sb[wv][e];
         if (i1 < 0 || better(v, e, v1, i1)) { v2 = v1; i2 = i1; v1 = v; i1 = e; }
         else if (i2 < 0 || better(v, e, v2, i2)) { v2 = v; i2 = e; }
       }
       gs[i] = (i2 >= 0) ? v1 + v2 : v1;
+      sg[wv][g] = gs[i];
     }
   }
-  // keep topk_group groups
-  bool keep[kMaxExpertsPerLane] = {false, false, false, false};
-  for (int k = 0; k < topk_group; ++k) {
-    float bv = ninf;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < kMaxExpertsPerLane; ++i) {
-      const int g = lane + 64 * i;
-      if (g < n_group && !keep[i] && better(gs[i], g, bv, bi)) { bv = gs[i]; bi = g; }
-    }
-    wave_argmax(bv, bi);
-#pragma unroll
-    for (int i = 0; i < kMaxExpertsPerLane; ++i)
-      if (lane + 64 * i == bi) keep[i] = true;
-  }
-  // the kept-group flag of each of this lane's experts
-  __shared__ int kg[4][256];
+  __syncthreads();
+  // a group is kept when fewer than topk_group groups come before it
 #pragma unroll
   for (int i = 0; i < kMaxExpertsPerLane; ++i) {
     const int g = lane + 64 * i;
-    if (g < n_group) kg[wv][g] = keep[i] ? 1 : 0;
+    if (g < n_group) {
+      int r = 0;
+#pragma unroll 8
+      for (int g2 = 0; g2 < n_group; ++g2) r += better(sg[wv][g2], g2, gs[i], g) ? 1 : 0;
+      kg[wv][g] = r < topk_group ? 1 : 0;
+    }
   }
   __syncthreads();
+  // compact the candidates in expert order
+  const uint64_t below = (1ull << lane) - 1ull;
+  int nc = 0;
   bool cand[kMaxExpertsPerLane];
+  int cpos[kMaxExpertsPerLane];
 #pragma unroll
   for (int i = 0; i < kMaxExpertsPerLane; ++i) {
     const int e = lane + 64 * i;
-    cand[i] = (e < E) && kg[wv][e / gsize];
+    cand[i] = (e < E) && kg[wv][e / gsize] != 0;
+    const uint64_t m = __ballot(cand[i]);
+    cpos[i] = nc + __popcll(m & below);
+    if (cand[i]) { cb[wv][cpos[i]] = b[i]; ce[wv][cpos[i]] = e; }
+    nc += __popcll(m);
   }
-  // top_k experts among the kept groups
-  float wsel = 0.0f;      // lane j < top_k ends up holding rank j's weight
-  int isel = 0;
-  for (int k = 0; k < top_k; ++k) {
-    float bv = ninf;
-    int bi = 0x7FFFFFFF;
-    float sv = 0.0f;
+  __syncthreads();
+  // a candidate is chosen at rank r = number of candidates before it
 #pragma unroll
-    for (int i = 0; i < kMaxExpertsPerLane; ++i) {
+  for (int i = 0; i < kMaxExpertsPerLane; ++i) {
+    if (cand[i]) {
       const int e = lane + 64 * i;
-      if (cand[i] && better(b[i], e, bv, bi)) { bv = b[i]; bi = e; }
+      int r = 0;
+#pragma unroll 8
+      for (int c = 0; c < nc; ++c) r += better(cb[wv][c], ce[wv][c], b[i], e) ? 1 : 0;
+      if (r < top_k) { sel_e[wv][r] = e; sel_s[wv][r] = s[i]; }
     }
-    wave_argmax(bv, bi);
-#pragma unroll
-    for (int i = 0; i < kMaxExpertsPerLane; ++i)
-      if (lane + 64 * i == bi) { cand[i] = false; sv = s[i]; }
-    // broadcast the chosen expert's unbiased score from its owner lane
-    sv = __shfl(sv, bi & 63, 64);
-    if (lane == k) { wsel = sv; isel = bi; }
   }
-  // normalize in rank order (sequential sum on lane 0), then scale
+  __syncthreads();
+  // normalize in rank order (every lane forms the same sequential sum), then scale
   float sum = 0.0f;
-  for (int k = 0; k < top_k; ++k) sum = sum + __shfl(wsel, k, 64);
+#pragma unroll 8
+  for (int k = 0; k < top_k; ++k) sum = sum + sel_s[wv][k];
   if (tv && lane < top_k) {
+    const float wsel = sel_s[wv][lane];
+    const int isel = sel_e[wv][lane];
     float wgt = norm ? wsel / sum : wsel;
     wgt = wgt * scaling;
     const int64_t p = (int64_t)t * top_k + lane;

@@ -330,6 +330,8 @@ int oracle_route(const float* logits, const float* bias, int tokens, int experts
     for (int e = 0; e < experts; ++e) {
       s[e] = oracle_sigmoid(logits[(int64_t)t * experts + e]);
       b[e] = s[e] + bias[e];
+      /* the pages give no order for NaN: a NaN score ranks below every number */
+      if (b[e] != b[e]) b[e] = -INFINITY;
     }
     /* group scores: sum of the two best biased scores (one if gsize == 1) */
     for (int g = 0; g < n_group; ++g) {

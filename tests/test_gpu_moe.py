@@ -70,6 +70,16 @@ def test_small_layers(nv, oracle, T, E, top_k, n_group, topk_group, hidden, inte
     _check(oracle, nv, c, top_k, n_group, topk_group)
 
 
+def test_nan_router_logits_rank_last(nv, oracle):
+    # a NaN score ranks below every number (the reading both sides implement)
+    c = _case(oracle, 64, 32, 128, 64, seed=21)
+    rng = np.random.default_rng(21)
+    lg = c["logits"].copy()
+    lg[rng.random(lg.shape) < 0.05] = np.nan
+    c["logits"] = lg
+    _check(oracle, nv, c, 4, 4, 2)
+
+
 def test_no_normalisation_and_scaling(nv, oracle):
     c = _case(oracle, 24, 16, 64, 64, seed=9)
     _check(oracle, nv, c, 4, 4, 2, norm=False, scaling=2.5)

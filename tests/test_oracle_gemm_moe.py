@@ -110,6 +110,22 @@ def test_route_exhaustive_small(oracle, E, n_group, topk_group, top_k):
         assert np.allclose(w[t], ws / ws.sum(), rtol=1e-6)
 
 
+def test_route_nan_scores_rank_last(oracle):
+    # NaN is given no order by the pages; the reading taken is that a NaN
+    # score ranks below every number (ties among them to the lower index)
+    logits = np.zeros((3, 8), np.float32)
+    logits[0, 0] = np.nan                 # would otherwise win the tie at index 0
+    logits[1, :] = np.nan                 # every score NaN: lowest indices of the kept group
+    logits[2, 5] = 4.0
+    logits[2, 4] = np.nan
+    bias = np.zeros(8, np.float32)
+    ids, w = oracle.route(logits, bias, 2, 2, 1, True, 1.0)
+    assert ids[0].tolist() == [1, 2]
+    assert ids[1].tolist() == [0, 1]
+    assert ids[2].tolist() == [5, 6]
+    assert np.all(np.isfinite(w[[0, 2]]))
+
+
 def test_route_ties_go_to_lower_index(oracle):
     logits = np.zeros((2, 16), np.float32)
     bias = np.zeros(16, np.float32)
