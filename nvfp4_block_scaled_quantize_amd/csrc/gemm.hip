@@ -99,7 +99,7 @@ constexpr int kSkKs = 4;          // K quarters per workgroup
 constexpr int kSkRows = 16 * kSkNsub;
 constexpr int kSkPF = 8;          // 128-k chunks loaded per round per wave
 constexpr int kSkItems = 16;      // activation items (8 codes) per thread
-constexpr int kSkEarly = 2;       // weight chunks loaded before the activation prologue
+constexpr int kSkEarly = 5;       // weight chunks loaded before the activation prologue
 constexpr size_t kSkRedBytes = (size_t)kSkKs * kSkRows * 16 * sizeof(float);
 
 // One workgroup = 8 waves = 2 sixteen-row weight subtiles x 4 K quarters.
@@ -112,7 +112,9 @@ constexpr size_t kSkRedBytes = (size_t)kSkKs * kSkRows * 16 * sizeof(float);
 //     barriers, which wait only for the issue of the few loads above (a wave
 //     whose weight loads are throttled by HBM would hold every barrier);
 //  3. the remaining weight loads of the round, then MFMAs chunk by chunk as the
-//     data arrives (in-order load counter);
+//     data arrives (in-order load counter).  The first round is straight-line
+//     code: inside a loop the compiler drained every outstanding load at the
+//     loop head, so the later chunks' loads waited a full memory latency;
 //  4. the four K quarters are summed in LDS in a fixed order.
 // A4: activation codes 4-byte aligned (dword loads), else byte loads.
 // NI: activation items (units of eight codes) per thread, >= B * ceil(K/8 / 512).
@@ -224,7 +226,7 @@ gemm_skinny(const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
   load_chunks(ks, kSkEarly, kSkPF);
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
   const _Float16* arow = As + (r16 < B ? r16 : B - 1) * pitch;
-  for (int c0 = ks;;) {
+  auto compute_round = [&](int c0) {
 #pragma unroll
     for (int i = 0; i < kSkPF; ++i) {
       const int c = c0 + i * kSkKs;
@@ -241,9 +243,13 @@ gemm_skinny(const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
           acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16(cw[m], m < 2 ? s0 : s1), bf[m], acc, 0, 0, 0);
       }
     }
-    c0 += kSkPF * kSkKs;
-    if (c0 >= nchunks) break;
+  };
+  // the first round straight-line (its loads were issued above), later rounds
+  // (K > 4096) in a loop
+  compute_round(ks);
+  for (int c0 = ks + kSkPF * kSkKs; c0 < nchunks; c0 += kSkPF * kSkKs) {
     load_chunks(c0, 0, kSkPF);
+    compute_round(c0);
   }
 
   // 4. sum the K quarters in a fixed order, scale, round to FP16
