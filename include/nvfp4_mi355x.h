@@ -26,7 +26,8 @@
  * Conventions for every call:
  *  - Pointers are DEVICE pointers unless stated; the caller allocates every
  *    buffer and keeps it alive until the stream work completes.  The library
- *    never allocates, frees or keeps a pointer past the call.
+ *    never allocates or frees, and keeps a pointer past the call only for a
+ *    registered external weight (until it is unregistered).
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Calls are asynchronous and stream-ordered; they never synchronize.
  *  - Arguments are validated on the host before anything is launched: on any
@@ -38,7 +39,8 @@
  *    results ("Building Custom TensorRT-LLM Plugins for Low-Latency FP8
  *    Inference at Scale", "Production Pitfalls & Hard Lessons", item 1).
  *  - Re-entrant; no mutable state besides a per-device property cache filled
- *    on first use.  Temporary memory comes from the caller's workspace
+ *    on first use and the external-weight registry (nvfp4_register_weight,
+ *    guarded by a lock).  Temporary memory comes from the caller's workspace
  *    (same article, item 3).
  */
 #ifndef NVFP4_MI355X_H
@@ -128,6 +130,41 @@ int32_t nvfp4_gemm(const uint8_t* a, const float* a_scale, const uint8_t* w, con
                    const float* w_gscale, void* y, int64_t B, int64_t N, int64_t K,
                    void* workspace, size_t workspace_bytes, void* stream);
 size_t nvfp4_gemm_workspace_size(int64_t B, int64_t N, int64_t K);
+
+/*
+ * External-weight mode of "Fused Nvfp4 GEMM All Reduce Plugin" (sections
+ * "External-weight inputs", "Attributes" and the register / unregister
+ * functions): the packed weight and its E4M3 block scale live outside the
+ * call, registered once per (device, resource id); the GEMM then names the
+ * resource instead of passing the two weight pointers.
+ *
+ * nvfp4_register_weight -- records (device, resource_id) -> (weight, scale,
+ * out_features = N, in_features = K, scale_cols = K/16).  Host-only: no HIP
+ * call, no copy; the pointers must stay valid for every GEMM that uses the
+ * resource, and the caller unregisters before releasing the storage.
+ *   weight : [N, K/2] uint8 device codes, 16-byte aligned
+ *   scale  : [N, K/16] uint8 device E4M3 bytes, 2-byte aligned
+ * Requires device >= 0, resource_id >= 0 (a negative id means baked-weight
+ * mode in the plugin and is rejected here), N > 0, K > 0, K % 32 == 0,
+ * scale_cols == K/16, and (device, resource_id) not registered yet; EINVAL
+ * otherwise (the registry is unchanged on error).
+ */
+int32_t nvfp4_register_weight(int32_t device, int32_t resource_id, const uint8_t* weight,
+                              const uint8_t* scale, int32_t out_features, int32_t in_features,
+                              int32_t scale_cols);
+/* Removes (device, resource_id); EINVAL if it is not registered. */
+int32_t nvfp4_unregister_weight(int32_t device, int32_t resource_id);
+/*
+ * nvfp4_gemm_external -- nvfp4_gemm with the weight and block scale of the
+ * resource registered for (current device, resource_id); the inputs are those
+ * of the plugin's external-weight mode: activation codes [B, K/2], combined
+ * activation scale [B, K/16], global weight scale (one device float).  N and
+ * K must equal the registered out/in features (EINVAL otherwise, as for an
+ * unknown resource).  Same kernels, results and workspace as nvfp4_gemm.
+ */
+int32_t nvfp4_gemm_external(const uint8_t* a, const float* a_scale, int32_t resource_id,
+                            const float* w_gscale, void* y, int64_t B, int64_t N, int64_t K,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * nvfp4_moe_w4a16 -- routed MoE layer with NVFP4 weights and FP16

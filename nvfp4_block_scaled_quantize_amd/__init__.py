@@ -22,6 +22,7 @@ ACT = {"none": 0, "swiglu": 1, "relu2": 2}
 EXPORTS = [
     "nvfp4_status_string", "nvfp4_quantize", "nvfp4_quantize_workspace_size", "nvfp4_act_quant",
     "nvfp4_gemm", "nvfp4_gemm_workspace_size", "nvfp4_moe_w4a16", "nvfp4_moe_w4a16_workspace_size",
+    "nvfp4_register_weight", "nvfp4_unregister_weight", "nvfp4_gemm_external",
 ]
 
 
@@ -54,6 +55,12 @@ def _load() -> ctypes.CDLL:
     L.nvfp4_moe_w4a16.restype = i32
     L.nvfp4_moe_w4a16_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     L.nvfp4_moe_w4a16_workspace_size.restype = sz
+    L.nvfp4_register_weight.argtypes = [i32, i32, p, p, i32, i32, i32]
+    L.nvfp4_register_weight.restype = i32
+    L.nvfp4_unregister_weight.argtypes = [i32, i32]
+    L.nvfp4_unregister_weight.restype = i32
+    L.nvfp4_gemm_external.argtypes = [p, p, i32, p, p, i64, i64, i64, p, sz, p]
+    L.nvfp4_gemm_external.restype = i32
     return L
 
 
@@ -159,6 +166,43 @@ def gemm(a_codes: torch.Tensor, a_scale: torch.Tensor, w_codes: torch.Tensor, w_
                          B, N, K, _ptr(ws), wsb, _stream(stream))
     if st != NVFP4_OK:
         raise Nvfp4Error(st, "nvfp4_gemm")
+    return y
+
+
+def register_weight(resource_id: int, w_codes: torch.Tensor, w_sf: torch.Tensor) -> None:
+    """Registers an external weight ([N, K/2] codes, [N, K/16] E4M3 bytes) for
+    (the tensors' device, resource_id).  The tensors must outlive the
+    registration: unregister before freeing them."""
+    _check_dev(w_codes, w_sf)
+    N, K = w_codes.shape[0], w_codes.shape[1] * 2
+    if w_sf.shape != (N, K // 16) or w_codes.dtype != torch.uint8 or w_sf.dtype != torch.uint8:
+        raise ValueError("weight shapes do not match the plugin contract")
+    st = _lib.nvfp4_register_weight(w_codes.device.index or 0, resource_id, _ptr(w_codes), _ptr(w_sf),
+                                    N, K, K // 16)
+    if st != NVFP4_OK:
+        raise Nvfp4Error(st, "nvfp4_register_weight")
+
+
+def unregister_weight(resource_id: int, device: int = 0) -> None:
+    st = _lib.nvfp4_unregister_weight(device, resource_id)
+    if st != NVFP4_OK:
+        raise Nvfp4Error(st, "nvfp4_unregister_weight")
+
+
+def gemm_external(a_codes: torch.Tensor, a_scale: torch.Tensor, resource_id: int, N: int,
+                  w_g: torch.Tensor, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """gemm() with the weight registered under resource_id on the current device."""
+    _check_dev(a_codes, a_scale, w_g)
+    B, K = a_codes.shape[0], a_codes.shape[1] * 2
+    if a_scale.shape != (B, K // 16) or a_scale.dtype != torch.float32 or w_g.dtype != torch.float32:
+        raise ValueError("activation operands do not match the plugin contract")
+    y = out if out is not None else torch.empty((B, N), dtype=torch.float16, device=a_codes.device)
+    ws, wsb = _workspace(gemm_workspace_size(B, N, K), a_codes.device, workspace)
+    st = _lib.nvfp4_gemm_external(_ptr(a_codes), _ptr(a_scale), resource_id, _ptr(w_g), _ptr(y),
+                                  B, N, K, _ptr(ws), wsb, _stream(stream))
+    if st != NVFP4_OK:
+        raise Nvfp4Error(st, "nvfp4_gemm_external")
     return y
 
 

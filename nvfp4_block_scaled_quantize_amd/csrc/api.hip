@@ -1,8 +1,10 @@
 // api.hip -- the C ABI of include/nvfp4_mi355x.h: host-side validation, the
-// per-device gfx950 check, workspace checks, and stream-ordered launches.
-// Nothing here allocates device memory, synchronizes, or keeps pointers.
+// per-device gfx950 check, workspace checks, stream-ordered launches and the
+// external-weight registry.  Nothing here allocates device memory or
+// synchronizes; only the registry keeps (caller-owned) pointers.
 #include <mutex>
 #include <string.h>
+#include <unordered_map>
 
 #include "../../include/nvfp4_mi355x.h"
 #include "internal.h"
@@ -41,6 +43,28 @@ int32_t device_status() {
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP; }
 
 bool aligned4(const void* p) { return ((uintptr_t)p % 4) == 0; }
+
+// External weights of "Fused Nvfp4 GEMM All Reduce Plugin" (external-weight
+// mode): (device, resource id) -> the caller's weight and scale pointers.
+struct ExternalWeight {
+  const uint8_t* weight;
+  const uint8_t* scale;
+  int32_t out_features, in_features;
+};
+
+struct Registry {
+  std::mutex mu;
+  std::unordered_map<uint64_t, ExternalWeight> map;
+};
+
+Registry& registry() {
+  static Registry r;
+  return r;
+}
+
+uint64_t registry_key(int32_t device, int32_t resource_id) {
+  return ((uint64_t)(uint32_t)device << 32) | (uint32_t)resource_id;
+}
 
 }  // namespace
 
@@ -128,6 +152,48 @@ int32_t nvfp4_gemm(const uint8_t* a, const float* a_scale, const uint8_t* w, con
   if (ds != NVFP4_OK) return ds;
   nvfp4::GemmArgs g{a, a_scale, w, w_sf, w_gscale, y, B, N, K, workspace, workspace_bytes};
   return hip_status(nvfp4::launch_gemm(g, (hipStream_t)stream));
+}
+
+int32_t nvfp4_register_weight(int32_t device, int32_t resource_id, const uint8_t* weight,
+                              const uint8_t* scale, int32_t out_features, int32_t in_features,
+                              int32_t scale_cols) {
+  if (device < 0 || resource_id < 0 || !weight || !scale) return NVFP4_EINVAL;
+  if (out_features <= 0 || in_features <= 0 || (in_features % 32) != 0 ||
+      scale_cols != in_features / 16)
+    return NVFP4_EINVAL;
+  if (((uintptr_t)weight % 16) != 0 || ((uintptr_t)scale % 2) != 0) return NVFP4_EINVAL;
+  Registry& r = registry();
+  std::lock_guard<std::mutex> lock(r.mu);
+  const bool inserted =
+      r.map.emplace(registry_key(device, resource_id),
+                    ExternalWeight{weight, scale, out_features, in_features}).second;
+  return inserted ? NVFP4_OK : NVFP4_EINVAL;
+}
+
+int32_t nvfp4_unregister_weight(int32_t device, int32_t resource_id) {
+  if (device < 0 || resource_id < 0) return NVFP4_EINVAL;
+  Registry& r = registry();
+  std::lock_guard<std::mutex> lock(r.mu);
+  return r.map.erase(registry_key(device, resource_id)) == 1 ? NVFP4_OK : NVFP4_EINVAL;
+}
+
+int32_t nvfp4_gemm_external(const uint8_t* a, const float* a_scale, int32_t resource_id,
+                            const float* w_gscale, void* y, int64_t B, int64_t N, int64_t K,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (resource_id < 0) return NVFP4_EINVAL;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return NVFP4_EHIP;
+  ExternalWeight ew;
+  {
+    Registry& r = registry();
+    std::lock_guard<std::mutex> lock(r.mu);
+    const auto it = r.map.find(registry_key(dev, resource_id));
+    if (it == r.map.end()) return NVFP4_EINVAL;
+    ew = it->second;
+  }
+  if (N != ew.out_features || K != ew.in_features) return NVFP4_EINVAL;
+  return nvfp4_gemm(a, a_scale, ew.weight, ew.scale, w_gscale, y, B, N, K, workspace,
+                    workspace_bytes, stream);
 }
 
 size_t nvfp4_moe_w4a16_workspace_size(int32_t tokens, int32_t experts, int32_t top_k,

@@ -85,3 +85,24 @@ def test_moe_validation_without_gpu(nv):
     assert L.nvfp4_moe_w4a16(*args, 4, 8, 2, 64, 32, 4, 2, 1, 1.0, None, 0, None) == nv.NVFP4_EINVAL
     # missing workspace
     assert L.nvfp4_moe_w4a16(*args, 4, 8, 2, 64, 64, 4, 2, 1, 1.0, None, 0, None) == nv.NVFP4_EWORKSPACE
+
+
+def test_external_weight_registry_without_gpu(nv):
+    # "Fused Nvfp4 GEMM All Reduce Plugin", external-weight mode: the registry
+    # is host-only, so it works (and validates) without a GPU
+    L = nv.lib()
+    w, s = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
+    assert L.nvfp4_register_weight(0, 7, w, s, 64, 128, 8) == nv.NVFP4_OK
+    assert L.nvfp4_register_weight(0, 7, w, s, 64, 128, 8) == nv.NVFP4_EINVAL      # already registered
+    assert L.nvfp4_register_weight(1, 7, w, s, 64, 128, 8) == nv.NVFP4_OK          # other device
+    assert L.nvfp4_register_weight(0, -1, w, s, 64, 128, 8) == nv.NVFP4_EINVAL     # baked-weight id
+    assert L.nvfp4_register_weight(0, 8, w, s, 64, 128, 4) == nv.NVFP4_EINVAL      # scale_cols != K/16
+    assert L.nvfp4_register_weight(0, 8, w, s, 64, 48, 3) == nv.NVFP4_EINVAL       # K % 32 != 0
+    assert L.nvfp4_register_weight(0, 8, ctypes.c_void_p(4104), s, 64, 128, 8) == nv.NVFP4_EINVAL
+    assert L.nvfp4_register_weight(0, 8, None, s, 64, 128, 8) == nv.NVFP4_EINVAL
+    assert L.nvfp4_unregister_weight(0, 7) == nv.NVFP4_OK
+    assert L.nvfp4_unregister_weight(0, 7) == nv.NVFP4_EINVAL
+    assert L.nvfp4_unregister_weight(1, 7) == nv.NVFP4_OK
+    assert L.nvfp4_unregister_weight(0, 8) == nv.NVFP4_EINVAL
+    p = ctypes.c_void_p(256)
+    assert L.nvfp4_gemm_external(p, p, -3, p, p, 4, 64, 128, None, 0, None) == nv.NVFP4_EINVAL

@@ -116,3 +116,27 @@ def test_deterministic(nv, oracle):
     y1 = _run(nv, qa, qw)
     y2 = _run(nv, qa, qw)
     assert np.array_equal(y1, y2)
+
+
+@pytest.mark.parametrize("B", [4, 64])
+def test_external_weight_mode_matches_baked(nv, oracle, B):
+    # "Fused Nvfp4 GEMM All Reduce Plugin", external-weight mode: same operands
+    # by registered resource id -> the same kernels, bit-identical output
+    N, K = 256, 512
+    a = si.bf16_normal((B, K), 1.0, 0, 0, 31)
+    wsrc = si.bf16_normal((N, K), 0.02, 0, 1, 31)
+    dev = "cuda"
+    qa = nv.quantize(a.to(dev))
+    qw = nv.quantize(wsrc.to(dev), group_rows=N, want_scale=False)
+    y0 = nv.gemm(qa["codes"], qa["scale"], qw["codes"], qw["sf"], qw["g_dec"])
+    nv.register_weight(41, qw["codes"], qw["sf"])
+    try:
+        y1 = nv.gemm_external(qa["codes"], qa["scale"], 41, N, qw["g_dec"])
+        torch.cuda.synchronize()
+        assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+        with pytest.raises(nv.Nvfp4Error):
+            nv.gemm_external(qa["codes"], qa["scale"], 41, N + 32, qw["g_dec"])   # N differs
+    finally:
+        nv.unregister_weight(41, torch.cuda.current_device())
+    with pytest.raises(nv.Nvfp4Error):
+        nv.gemm_external(qa["codes"], qa["scale"], 41, N, qw["g_dec"])
