@@ -553,6 +553,8 @@ gemm_wide(const _Float16* __restrict__ a16, const float* __restrict__ rowscale,
 
   // DMA work of this wave per stage: A blocks 2w, 2w+1 (8 rows each), W rows
   // 64w .. 64w+63 (two copies of 32 rows), E4M3 bytes of rows 64w .. 64w+63.
+  // The tile's first row goes into the 64-bit scalar base; the 32-bit lane
+  // offsets are relative to it (< 512 rows x K bytes), so no size wraps.
   uint32_t aofs[2], wofs[2], sofs;
   int alds[2], wlds[2], slds;
 #pragma unroll
@@ -561,7 +563,7 @@ gemm_wide(const _Float16* __restrict__ a16, const float* __restrict__ rowscale,
     {
       int r = m0 + 8 * blk + r8;
       r = r < B ? r : B - 1;
-      aofs[j] = (uint32_t)r * (uint32_t)K * 2u + 16u * c;
+      aofs[j] = (uint32_t)(r - m0) * (uint32_t)K * 2u + 16u * c;
       alds[j] = kXAOff + (wave * 2 + j) * 1024;
     }
   }
@@ -570,16 +572,18 @@ gemm_wide(const _Float16* __restrict__ a16, const float* __restrict__ rowscale,
     const int rl = 64 * wave + 32 * j + (lane >> 1);
     int r = n0 + rl;
     r = r < N ? r : N - 1;
-    wofs[j] = (uint32_t)r * (uint32_t)(K / 2) + 16u * ((lane & 1) ^ (((rl >> 2) ^ (rl >> 3)) & 1));
+    wofs[j] = (uint32_t)(r - n0) * (uint32_t)(K / 2) + 16u * ((lane & 1) ^ (((rl >> 2) ^ (rl >> 3)) & 1));
     wlds[j] = kXWOff + (wave * 2 + j) * 1024;
   }
   {
     int r = n0 + 64 * wave + lane;
     r = r < N ? r : N - 1;
-    sofs = (uint32_t)r * (uint32_t)(K / 16);
+    sofs = (uint32_t)(r - n0) * (uint32_t)(K / 16);
     slds = kXSOff + wave * 256;
   }
-  const unsigned char* abase = reinterpret_cast<const unsigned char*>(a16);
+  const unsigned char* abase = reinterpret_cast<const unsigned char*>(a16) + (size_t)m0 * K * 2;
+  const uint8_t* wbase = w + (size_t)n0 * (K / 2);
+  const uint8_t* sbase = w_sf + (size_t)n0 * (K / 16);
 
   auto issue = [&](unsigned char* buf, int st) {
     const int k0 = st * kTK;
@@ -588,8 +592,8 @@ gemm_wide(const _Float16* __restrict__ a16, const float* __restrict__ rowscale,
 #pragma unroll
     for (int j = 0; j < 2; ++j) dma16(ab, aofs[j], l0 + alds[j]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) dma16(w + k0 / 2, wofs[j], l0 + wlds[j]);
-    dma4(w_sf + k0 / 16, sofs, l0 + slds);
+    for (int j = 0; j < 2; ++j) dma16(wbase + k0 / 2, wofs[j], l0 + wlds[j]);
+    dma4(sbase + k0 / 16, sofs, l0 + slds);
   };
   constexpr int kLoads = 5;   // per wave per stage
 
@@ -716,7 +720,8 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   float* rowscale = reinterpret_cast<float*>(ws + align256((size_t)B * (size_t)K * 2));
   hipLaunchKernelGGL(a_to_f16_rows, dim3((unsigned)B), dim3(256), 0, s, g.a, g.a_scale, a16,
                      rowscale, K);
-  if (K % kTK == 0 && ((uintptr_t)g.w_sf % 4) == 0) {
+  // gemm_wide's copies take 32-bit lane offsets of up to 512 rows x K bytes
+  if (K % kTK == 0 && ((uintptr_t)g.w_sf % 4) == 0 && g.K <= (1 << 24)) {
     const int wtm = (B + kXM - 1) / kXM, wtn = (N + kXN - 1) / kXN;
     hipLaunchKernelGGL(gemm_wide, dim3((unsigned)(wtm * wtn)), dim3(kP2Threads), 0, s, a16,
                        rowscale, g.w, g.w_sf, g.w_g, y, B, N, K, wtm, wtn);

@@ -101,3 +101,22 @@ def moe_inputs(seed: int = SEED, T=None, E=None, hidden=None, inter=None, weight
     w1 = bf16_normal((E * inter, hidden), c["w_std"], "C5", 1, seed) if weights else None
     w2 = bf16_normal((E * hidden, inter), c["w_std"], "C5", 2, seed) if weights else None
     return dict(logits=logits, bias=bias, x=x, w1=w1, w2=w2, T=T, E=E, hidden=hidden, inter=inter)
+
+
+def random_nvfp4_operands(B: int, N: int, K: int, seed: int = SEED, config: int = 60) -> dict:
+    """Arbitrary valid GEMM operands drawn directly in the stored formats (no
+    quantization involved): uniform code bytes, positive finite combined
+    activation scales with a uniform exponent in [-10, 2] and uniform
+    mantissa bits, E4M3 weight scale bytes 0x00..0x7E (positive, finite) and
+    a global weight scale.  For size tests where quantizing a real input on
+    the CPU would be too slow."""
+    g = rng(config, 0, seed)
+    ex = g.integers(127 - 10, 127 + 3, size=(B, K // 16), dtype=np.uint8).astype(np.uint32)
+    mant = g.integers(0, 1 << 23, size=(B, K // 16), dtype=np.uint32)
+    return {
+        "a_codes": g.integers(0, 256, size=(B, K // 2), dtype=np.uint8),
+        "a_scale": (np.left_shift(ex, 23) | mant).view(np.float32),
+        "w_codes": g.integers(0, 256, size=(N, K // 2), dtype=np.uint8),
+        "w_sf": g.integers(0, 0x7F, size=(N, K // 16), dtype=np.uint8),
+        "w_g": np.array([1.0 / 2688.0], np.float32),
+    }

@@ -140,3 +140,20 @@ def test_external_weight_mode_matches_baked(nv, oracle, B):
         nv.unregister_weight(41, torch.cuda.current_device())
     with pytest.raises(nv.Nvfp4Error):
         nv.gemm_external(qa["codes"], qa["scale"], 41, N, qw["g_dec"])
+
+
+def test_prefill_path_past_4gib_of_fp16_activations(nv, oracle):
+    # B*K*2 > 4 GiB: the copy offsets of the prefill kernel must not wrap
+    # (rows past 32768 are checked); ragged in B (not a multiple of 128) and N
+    B, N, K = 33024, 96, 65536
+    d = si.random_nvfp4_operands(B, N, K, seed=5)
+    dev = "cuda"
+    t = {k: torch.from_numpy(v).to(dev) for k, v in d.items()}
+    y = nv.gemm(t["a_codes"], t["a_scale"], t["w_codes"], t["w_sf"], t["w_g"])
+    torch.cuda.synchronize()
+    rows = [0, 127, 128, 32767, 32768, 32900, B - 1]
+    got = y[rows].cpu().double().numpy()
+    ref = oracle.gemm_ref(d["a_codes"], d["a_scale"], d["w_codes"], d["w_sf"], d["w_g"][0], rows=rows)
+    assert oracle.rel_fro(got, ref) <= TOL
+    del t, y
+    torch.cuda.empty_cache()
