@@ -344,7 +344,15 @@ moe_fc_wide(const _Float16* __restrict__ act, const int32_t* __restrict__ plists
   __shared__ float redmax[FC == 1 ? kFwThreads / 64 : 1][kFwTok];   // fc1: per-wave largest h
   // fc2: factor 2^(et - e) of each fc1 row tile t of each slot's pair
   __shared__ _Float16 sfac[FC == 2 ? kFwMaxT1 : 1][kFwTok];
-  const int e = blockIdx.y;
+  // workgroups of one expert on one XCD (consecutive workgroup ids go to
+  // consecutive XCDs), so the expert's activations are fetched into one L2
+  int bx = blockIdx.x, e = blockIdx.y;
+  if ((gridDim.y & 7) == 0) {
+    const int L = blockIdx.x + gridDim.x * blockIdx.y;
+    const int slot = L >> 3;
+    bx = slot % gridDim.x;
+    e = (slot / gridDim.x) * 8 + (L & 7);
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int32_t* pl = plists + (int64_t)e * T;
   const int32_t* tl = tlists + (int64_t)e * T;
@@ -363,7 +371,7 @@ moe_fc_wide(const _Float16* __restrict__ act, const int32_t* __restrict__ plists
   const int nch = (K + kFwKC - 1) / kFwKC;
   const int nchp = (nch + kFwWBuf - 1) / kFwWBuf * kFwWBuf;   // whole rounds of four (extra chunks are zero)
   const int tiles = (N + kFwRows - 1) / kFwRows;
-  const int xt0 = blockIdx.x * R;
+  const int xt0 = bx * R;
   const int ntile = (tiles - xt0 < R) ? tiles - xt0 : R;
   const float ge = w_g[e];
   const uint8_t* we = w + (int64_t)e * N * (K / 2);
