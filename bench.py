@@ -3,10 +3,12 @@
 
 A step is one pass of the path over one batch: per-token NVFP4 quantization
 of the activations (nvfp4_act_quant) followed by the block-scaled NVFP4 GEMM
-(nvfp4_gemm) against pre-quantized weights.  The headline workload is the
+against weights prepared offline (quantized per tensor and pre-tiled by
+nvfp4_pretile_weight; nvfp4_gemm_pretiled).  The headline workload is the
 prefill GEMM B=4096, K=8192, N=8192 (bf16 activations ~N(0,1), weights
-~N(0,0.02) quantized per tensor, FP16 output); `value` is whole-step TFLOP/s
-(2*B*N*K per step).  The other workloads (decode GEMM, fused SwiGLU quantize,
+~N(0,0.02), FP16 output); `value` is whole-step TFLOP/s (2*B*N*K per step).
+The same GEMM on the plain [N, K/2] weight layout (nvfp4_gemm) is timed after
+the steps and reported under "workloads".  The other workloads (decode GEMM, fused SwiGLU quantize,
 quantize + GEMM small case, MoE) are measured after it and reported under
 "workloads".
 
@@ -88,7 +90,10 @@ def run_prefill(torch, nv, si, steps, warmup):
     dev = torch.device("cuda:0")
     a, w = si.gemm_inputs("C3")
     x = a.to(dev)
+    # offline weight preparation (not timed): NVFP4 quantization per tensor,
+    # then the pre-tiled layout the GEMM's lanes read (nvfp4_pretile_weight)
     wq = nv.quantize(w.to(dev), group_rows=N, want_scale=False)
+    wt = nv.pretile_weight(wq["codes"], wq["sf"])
     del w
     stream = torch.cuda.current_stream()
     qa = {"codes": torch.empty((B, K // 2), dtype=torch.uint8, device=dev),
@@ -100,7 +105,7 @@ def run_prefill(torch, nv, si, steps, warmup):
 
     def step(tq=None, tg=None):
         fq = lambda: nv.act_quant(x, "none", out=qa)
-        fg = lambda: nv.gemm(qa["codes"], qa["scale"], wq["codes"], wq["sf"], wq["g_dec"], out=y, workspace=ws)
+        fg = lambda: nv.gemm_pretiled(qa["codes"], qa["scale"], wt, wq["g_dec"], out=y, workspace=ws)
         tq(fq) if tq else fq()
         tg(fg) if tg else fg()
 
@@ -118,7 +123,14 @@ def run_prefill(torch, nv, si, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / steps
+    # the same GEMM on the weights in the plain [N, K/2] layout (nvfp4_gemm)
+    tu = EventTimer(torch, stream)
+    for i in range(warmup + steps):
+        f = lambda: nv.gemm(qa["codes"], qa["scale"], wq["codes"], wq["sf"], wq["g_dec"], out=y, workspace=ws)
+        tu(f) if i >= warmup else f()
+    torch.cuda.synchronize()
     return dict(B=B, K=K, N=N, ms_step=ms_step, wall_s=wall, ms_gemm=tg.mean_ms(), ms_quant=tq.mean_ms(),
+                ms_gemm_untiled=tu.mean_ms(),
                 flops=2.0 * B * N * K, qbytes=quant_bytes(B, K, K), gbytes=gemm_bytes(B, N, K))
 
 
@@ -163,9 +175,15 @@ def run_decode(torch, nv, si, B, iters=None):
     y = torch.empty((B, N), dtype=torch.float16, device=dev)
     ms_gemm = graph_time_ms(torch, [(lambda Wi=Wi: nv.gemm(qa["codes"], qa["scale"], *Wi, out=y)) for Wi in Ws])
     ms_quant = graph_time_ms(torch, [lambda: nv.act_quant(x, "none", out=qa)] * 8)
+    # the same weights pre-tiled offline (nvfp4_pretile_weight)
+    Wt = [(nv.pretile_weight(Wi[0], Wi[1]), Wi[2]) for Wi in Ws]
+    del Ws
+    ms_tiled = graph_time_ms(torch, [(lambda Wi=Wi: nv.gemm_pretiled(qa["codes"], qa["scale"], Wi[0], Wi[1], out=y))
+                                     for Wi in Wt])
     gb = gemm_bytes(B, N, K)
     return dict(B=B, us_gemm=ms_gemm * 1e3, us_quant=ms_quant * 1e3, gemm_bytes=gb,
-                gemm_GBps=gb / (ms_gemm * 1e-3) / 1e9, hbm_frac=gb / (ms_gemm * 1e-3) / 1e9 / HBM_PEAK_GBS)
+                gemm_GBps=gb / (ms_gemm * 1e-3) / 1e9, hbm_frac=gb / (ms_gemm * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                us_gemm_pretiled=ms_tiled * 1e3, hbm_frac_pretiled=gb / (ms_tiled * 1e-3) / 1e9 / HBM_PEAK_GBS)
 
 
 def run_quant_rotating(torch, nv, si, copies=5, reps=4):
@@ -326,7 +344,9 @@ def main():
         "gemm_frac_fp16_peak": round(gemm_tflops / FP16_MFMA_PEAK_TFLOPS, 4),
         "gemm_frac_fp4_peak": round(gemm_tflops / FP4_MFMA_PEAK_TFLOPS, 4),
         "act_quant_ms": round(pre["ms_quant"], 4), "act_quant_GBps": round(quant_gbs, 1),
-        "act_quant_hbm_frac": round(quant_gbs / HBM_PEAK_GBS, 4)}}
+        "act_quant_hbm_frac": round(quant_gbs / HBM_PEAK_GBS, 4),
+        "gemm_untiled_ms": round(pre["ms_gemm_untiled"], 4),
+        "gemm_untiled_TFLOPs": round(pre["flops"] / (pre["ms_gemm_untiled"] * 1e-3) / 1e12, 1)}}
     if not args.quick:
         for B in (1, 4, 8):
             log("decode B=%d" % B)
@@ -356,10 +376,11 @@ def main():
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(pre["ms_step"], 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
-        "data": "synthetic (seeded bf16 normals; weights quantized to NVFP4 on the GPU before timing)",
+        "data": "synthetic (seeded bf16 normals; weights quantized to NVFP4 and pre-tiled on the GPU before timing)",
         "config": {"workload": "prefill: per-token act quantize [4096,8192] + NVFP4 GEMM B=4096 K=8192 N=8192",
                    "B": pre["B"], "K": pre["K"], "N": pre["N"], "parallelism": "single GPU"},
-        "roofline": {"kernel": "nvfp4_gemm (prefill)", "bound": "mfma", "achieved": round(gemm_tflops, 1),
+        "roofline": {"kernel": "nvfp4_gemm_pretiled (prefill: a_to_f16_rows + gemm_wide<true>)", "bound": "mfma",
+                     "achieved": round(gemm_tflops, 1),
                      "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / FP16_MFMA_PEAK_TFLOPS, 4),
                      "traffic": load_traffic(), "traffic_unit": "bytes per call"},

@@ -132,6 +132,39 @@ int32_t nvfp4_gemm(const uint8_t* a, const float* a_scale, const uint8_t* w, con
 size_t nvfp4_gemm_workspace_size(int64_t B, int64_t N, int64_t K);
 
 /*
+ * Pre-tiled weights: the offline reordering of the weight codes and E4M3
+ * bytes into the order the GEMM's lanes read them -- the role of the baked
+ * N128_K64 weight tiling of "Nvfp4 A16 Blackwell Moe Runner" (fc1/fc2 weight
+ * layout) and of the weight shuffles of "feature: add fp4 mm using trtllm
+ * backend", done for gfx950's lanes.  Layout: row group G = rows 16G..16G+15;
+ * for each 128-k chunk c a 1 KiB tile of codes whose 16-byte lane l = r + 16q
+ * (r < 16, q < 4) holds the 32 codes of row 16G + r at k = 128c + 32q .. +31
+ * (same packing as [N, K/2]), and a 128-byte tile of E4M3 bytes whose 2-byte
+ * lane l holds that row's two block scales for those 32 k.  Tiles are stored
+ * row group by row group, chunk by chunk: codes [N/16][K/128][64][16 B] (N*K/2
+ * bytes), E4M3 bytes [N/16][K/128][64][2 B] (N*K/16 bytes).
+ *
+ * nvfp4_pretile_weight -- writes that layout from [N, K/2] codes and
+ * [N, K/16] E4M3 bytes (a permutation; the inputs are not modified).
+ *   w_tiled : N*K/2 bytes, 16-byte aligned; sf_tiled: N*K/16 bytes, 4-byte aligned
+ * Requires N % 16 == 0, K % 128 == 0, K <= 2^24; w 16-byte and w_sf 2-byte
+ * aligned (EINVAL / EUNSUPPORTED otherwise).
+ */
+int32_t nvfp4_pretile_weight(const uint8_t* w, const uint8_t* w_sf, int64_t N, int64_t K,
+                             uint8_t* w_tiled, uint8_t* sf_tiled, void* stream);
+/*
+ * nvfp4_gemm_pretiled -- nvfp4_gemm with the weight operands in the
+ * pre-tiled layout.  Same arithmetic and results as nvfp4_gemm on the
+ * untiled weights (bit-identical output), same workspace
+ * (nvfp4_gemm_workspace_size).  Requires N % 16 == 0, K % 128 == 0,
+ * K <= 2^24, w_tiled 16-byte and sf_tiled 4-byte aligned.
+ */
+int32_t nvfp4_gemm_pretiled(const uint8_t* a, const float* a_scale, const uint8_t* w_tiled,
+                            const uint8_t* sf_tiled, const float* w_gscale, void* y, int64_t B,
+                            int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
  * External-weight mode of "Fused Nvfp4 GEMM All Reduce Plugin" (sections
  * "External-weight inputs", "Attributes" and the register / unregister
  * functions): the packed weight and its E4M3 block scale live outside the

@@ -23,6 +23,7 @@ EXPORTS = [
     "nvfp4_status_string", "nvfp4_quantize", "nvfp4_quantize_workspace_size", "nvfp4_act_quant",
     "nvfp4_gemm", "nvfp4_gemm_workspace_size", "nvfp4_moe_w4a16", "nvfp4_moe_w4a16_workspace_size",
     "nvfp4_register_weight", "nvfp4_unregister_weight", "nvfp4_gemm_external",
+    "nvfp4_pretile_weight", "nvfp4_gemm_pretiled",
 ]
 
 
@@ -61,6 +62,10 @@ def _load() -> ctypes.CDLL:
     L.nvfp4_unregister_weight.restype = i32
     L.nvfp4_gemm_external.argtypes = [p, p, i32, p, p, i64, i64, i64, p, sz, p]
     L.nvfp4_gemm_external.restype = i32
+    L.nvfp4_pretile_weight.argtypes = [p, p, i64, i64, p, p, p]
+    L.nvfp4_pretile_weight.restype = i32
+    L.nvfp4_gemm_pretiled.argtypes = [p, p, p, p, p, p, i64, i64, i64, p, sz, p]
+    L.nvfp4_gemm_pretiled.restype = i32
     return L
 
 
@@ -166,6 +171,39 @@ def gemm(a_codes: torch.Tensor, a_scale: torch.Tensor, w_codes: torch.Tensor, w_
                          B, N, K, _ptr(ws), wsb, _stream(stream))
     if st != NVFP4_OK:
         raise Nvfp4Error(st, "nvfp4_gemm")
+    return y
+
+
+def pretile_weight(w_codes: torch.Tensor, w_sf: torch.Tensor, stream=None) -> dict:
+    """The pre-tiled layout of [N, K/2] codes and [N, K/16] E4M3 bytes (flat
+    uint8 tensors of N*K/2 and N*K/16 bytes)."""
+    _check_dev(w_codes, w_sf)
+    N, K = w_codes.shape[0], w_codes.shape[1] * 2
+    if w_sf.shape != (N, K // 16) or w_codes.dtype != torch.uint8 or w_sf.dtype != torch.uint8:
+        raise ValueError("weight shapes do not match the plugin contract")
+    wt = torch.empty(N * K // 2, dtype=torch.uint8, device=w_codes.device)
+    st = torch.empty(N * K // 16, dtype=torch.uint8, device=w_codes.device)
+    rc = _lib.nvfp4_pretile_weight(_ptr(w_codes), _ptr(w_sf), N, K, _ptr(wt), _ptr(st), _stream(stream))
+    if rc != NVFP4_OK:
+        raise Nvfp4Error(rc, "nvfp4_pretile_weight")
+    return {"codes": wt, "sf": st, "N": N, "K": K}
+
+
+def gemm_pretiled(a_codes: torch.Tensor, a_scale: torch.Tensor, wt: dict, w_g: torch.Tensor,
+                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                  stream=None) -> torch.Tensor:
+    """gemm() with weights from pretile_weight()."""
+    _check_dev(a_codes, a_scale, w_g, wt["codes"], wt["sf"])
+    B, K = a_codes.shape[0], a_codes.shape[1] * 2
+    N = wt["N"]
+    if K != wt["K"] or a_scale.shape != (B, K // 16) or a_scale.dtype != torch.float32:
+        raise ValueError("operand shapes do not match the plugin contract")
+    y = out if out is not None else torch.empty((B, N), dtype=torch.float16, device=a_codes.device)
+    ws, wsb = _workspace(gemm_workspace_size(B, N, K), a_codes.device, workspace)
+    rc = _lib.nvfp4_gemm_pretiled(_ptr(a_codes), _ptr(a_scale), _ptr(wt["codes"]), _ptr(wt["sf"]), _ptr(w_g),
+                                  _ptr(y), B, N, K, _ptr(ws), wsb, _stream(stream))
+    if rc != NVFP4_OK:
+        raise Nvfp4Error(rc, "nvfp4_gemm_pretiled")
     return y
 
 

@@ -150,7 +150,38 @@ int32_t nvfp4_gemm(const uint8_t* a, const float* a_scale, const uint8_t* w, con
   if (need > 0 && (!workspace || workspace_bytes < need)) return NVFP4_EWORKSPACE;
   const int32_t ds = device_status();
   if (ds != NVFP4_OK) return ds;
-  nvfp4::GemmArgs g{a, a_scale, w, w_sf, w_gscale, y, B, N, K, workspace, workspace_bytes};
+  nvfp4::GemmArgs g{a, a_scale, w, w_sf, w_gscale, y, B, N, K, workspace, workspace_bytes, 0};
+  return hip_status(nvfp4::launch_gemm(g, (hipStream_t)stream));
+}
+
+int32_t nvfp4_pretile_weight(const uint8_t* w, const uint8_t* w_sf, int64_t N, int64_t K,
+                             uint8_t* w_tiled, uint8_t* sf_tiled, void* stream) {
+  if (N <= 0 || K <= 0 || (N % 16) != 0 || (K % 128) != 0) return NVFP4_EINVAL;
+  if (!w || !w_sf || !w_tiled || !sf_tiled) return NVFP4_EINVAL;
+  if (((uintptr_t)w % 16) != 0 || ((uintptr_t)w_tiled % 16) != 0 || ((uintptr_t)w_sf % 2) != 0 ||
+      ((uintptr_t)sf_tiled % 4) != 0)
+    return NVFP4_EINVAL;
+  if (N > 0x7FFFFFFFLL || K > (1LL << 24)) return NVFP4_EUNSUPPORTED;
+  const int32_t ds = device_status();
+  if (ds != NVFP4_OK) return ds;
+  return hip_status(nvfp4::launch_pretile(w, w_sf, N, K, w_tiled, sf_tiled, (hipStream_t)stream));
+}
+
+int32_t nvfp4_gemm_pretiled(const uint8_t* a, const float* a_scale, const uint8_t* w_tiled,
+                            const uint8_t* sf_tiled, const float* w_gscale, void* y, int64_t B,
+                            int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (B < 0 || N <= 0 || K <= 0 || (N % 16) != 0 || (K % 128) != 0) return NVFP4_EINVAL;
+  if (B == 0) return NVFP4_OK;
+  if (!a || !a_scale || !w_tiled || !sf_tiled || !w_gscale || !y) return NVFP4_EINVAL;
+  if (!aligned4(a_scale) || !aligned4(w_gscale) || ((uintptr_t)y % 2) != 0) return NVFP4_EINVAL;
+  if (((uintptr_t)w_tiled % 16) != 0 || ((uintptr_t)sf_tiled % 4) != 0) return NVFP4_EINVAL;
+  if (B > 0x7FFFFFFFLL || N > 0x7FFFFFFFLL || K > (1LL << 24)) return NVFP4_EUNSUPPORTED;
+  const size_t need = nvfp4::gemm_workspace_bytes(B, N, K);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return NVFP4_EWORKSPACE;
+  const int32_t ds = device_status();
+  if (ds != NVFP4_OK) return ds;
+  nvfp4::GemmArgs g{a, a_scale, w_tiled, sf_tiled, w_gscale, y, B, N, K, workspace, workspace_bytes, 1};
   return hip_status(nvfp4::launch_gemm(g, (hipStream_t)stream));
 }
 

@@ -118,7 +118,10 @@ constexpr size_t kSkRedBytes = (size_t)kSkKs * kSkRows * 16 * sizeof(float);
 //  4. the four K quarters are summed in LDS in a fixed order.
 // A4: activation codes 4-byte aligned (dword loads), else byte loads.
 // NI: activation items (units of eight codes) per thread, >= B * ceil(K/8 / 512).
-template <bool A4, int NI>
+// TILED: the weights are in the pre-tiled layout (nvfp4_pretile_weight): each
+// wave-load of 16 rows x 128 k is one contiguous KiB (codes) / 128 B (E4M3
+// bytes) instead of 16 row segments.
+template <bool A4, int NI, bool TILED>
 __global__ void __launch_bounds__(kSkThreads)
 gemm_skinny(const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
             const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_sf,
@@ -174,10 +177,17 @@ gemm_skinny(const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
     for (int i = 0; i < kSkPF; ++i) {
       if (i < i0 || i >= i1) continue;
       const int c = c0 + i * kSkKs;
-      const int k0 = c * 128 + 32 * g;
-      const int k = (c < nchunks && k0 < K) ? k0 : 0;
-      wc[i] = *reinterpret_cast<const uint4*>(wr + k / 2);
-      wsv[i] = (uint32_t)*reinterpret_cast<const uint16_t*>(sr + k / 16);
+      if constexpr (TILED) {
+        // tile (row group, chunk), lane order r16 + 16 g (K % 128 == 0)
+        const int64_t t = ((int64_t)(nrow < N ? nrow : N - 1) / 16 * nchunks + (c < nchunks ? c : 0)) * 64 + lane;
+        wc[i] = *reinterpret_cast<const uint4*>(w + t * 16);
+        wsv[i] = (uint32_t)*reinterpret_cast<const uint16_t*>(w_sf + t * 2);
+      } else {
+        const int k0 = c * 128 + 32 * g;
+        const int k = (c < nchunks && k0 < K) ? k0 : 0;
+        wc[i] = *reinterpret_cast<const uint4*>(wr + k / 2);
+        wsv[i] = (uint32_t)*reinterpret_cast<const uint16_t*>(sr + k / 16);
+      }
     }
   };
   load_chunks(ks, 0, kSkEarly);
@@ -272,15 +282,18 @@ typedef void (*SkinnyFn)(const uint8_t*, const float*, const uint8_t*, const uin
                          _Float16*, int, int, int);
 
 // The instantiation with the fewest activation items per thread covering ni.
-template <bool A4>
+template <bool A4, bool TILED>
 SkinnyFn skinny_kernel_a(int ni) {
-  if (ni <= 1) return gemm_skinny<A4, 1>;
-  if (ni <= 2) return gemm_skinny<A4, 2>;
-  if (ni <= 4) return gemm_skinny<A4, 4>;
-  if (ni <= 8) return gemm_skinny<A4, 8>;
-  return gemm_skinny<A4, kSkItems>;
+  if (ni <= 1) return gemm_skinny<A4, 1, TILED>;
+  if (ni <= 2) return gemm_skinny<A4, 2, TILED>;
+  if (ni <= 4) return gemm_skinny<A4, 4, TILED>;
+  if (ni <= 8) return gemm_skinny<A4, 8, TILED>;
+  return gemm_skinny<A4, kSkItems, TILED>;
 }
-SkinnyFn skinny_kernel(bool a4, int ni) { return a4 ? skinny_kernel_a<true>(ni) : skinny_kernel_a<false>(ni); }
+SkinnyFn skinny_kernel(bool a4, int ni, bool tiled) {
+  if (tiled) return a4 ? skinny_kernel_a<true, true>(ni) : skinny_kernel_a<false, true>(ni);
+  return a4 ? skinny_kernel_a<true, false>(ni) : skinny_kernel_a<false, false>(ni);
+}
 
 size_t skinny_lds_bytes(int64_t B, int64_t K) {
   return (((size_t)B * (size_t)(K + 8) * 2 + 15) / 16) * 16 + kSkRedBytes;
@@ -310,12 +323,12 @@ a_to_f16_rows(const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
   const float inv = __builtin_ldexpf(1.0f, -e);
   if (threadIdx.x == 0) rowscale[row] = __builtin_ldexpf(1.0f, e);
   const uint8_t* ar = a + row * (K / 2);
-  _Float16* out = a16 + row * K;
   for (int64_t j = threadIdx.x; j < kb16; j += 256) {
     const float c = sc[j] * inv;
     const uint32_t c0 = load_u32_bytes(ar + 8 * j), c1 = load_u32_bytes(ar + 8 * j + 4);
-    *reinterpret_cast<v8h*>(out + 16 * j) = dequant8_act(c0, c);
-    *reinterpret_cast<v8h*>(out + 16 * j + 8) = dequant8_act(c1, c);
+    _Float16* out = a16 + row * K + 16 * j;
+    *reinterpret_cast<v8h*>(out) = dequant8_act(c0, c);
+    *reinterpret_cast<v8h*>(out + 8) = dequant8_act(c1, c);
   }
 }
 
@@ -518,6 +531,11 @@ constexpr int kXWOff = kXAOff + kXM * 128;         // W: 512 rows x 32 B
 constexpr int kXSOff = kXWOff + kXN * 32;          // S: 512 rows x 4 B
 constexpr int kXStage = kXSOff + kXN * 4;
 
+// TILED: weights in the pre-tiled layout, where the 16 rows of a row group
+// are interleaved so that one 64-k stage of a row group is one contiguous
+// 512 B (codes) / 64 B (E4M3 bytes); the copies then read 512 B segments and
+// the LDS holds each row group in that order (row r16 + 16 h, h = 32-k half).
+template <bool TILED>
 __global__ void __launch_bounds__(kP2Threads)
 gemm_wide(const _Float16* __restrict__ a16, const float* __restrict__ rowscale,
           const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_sf,
@@ -567,19 +585,37 @@ gemm_wide(const _Float16* __restrict__ a16, const float* __restrict__ rowscale,
       alds[j] = kXAOff + (wave * 2 + j) * 1024;
     }
   }
+  if constexpr (TILED) {
+    // row group G of the tile (16 rows): K*8 bytes of codes, K bytes of
+    // E4M3 bytes; stage st at st*512 / st*64 inside it
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int rl = 64 * wave + 32 * j + (lane >> 1);
-    int r = n0 + rl;
-    r = r < N ? r : N - 1;
-    wofs[j] = (uint32_t)(r - n0) * (uint32_t)(K / 2) + 16u * ((lane & 1) ^ (((rl >> 2) ^ (rl >> 3)) & 1));
-    wlds[j] = kXWOff + (wave * 2 + j) * 1024;
-  }
-  {
-    int r = n0 + 64 * wave + lane;
-    r = r < N ? r : N - 1;
-    sofs = (uint32_t)(r - n0) * (uint32_t)(K / 16);
-    slds = kXSOff + wave * 256;
+    for (int j = 0; j < 2; ++j) {
+      int grp = n0 / 16 + (wave * 2 + j) * 2 + (lane >> 5);
+      grp = grp < N / 16 ? grp : N / 16 - 1;
+      wofs[j] = (uint32_t)(grp - n0 / 16) * (uint32_t)K * 8u + 16u * (lane & 31);
+      wlds[j] = kXWOff + (wave * 2 + j) * 1024;
+    }
+    {
+      int grp = n0 / 16 + wave * 4 + (lane >> 4);
+      grp = grp < N / 16 ? grp : N / 16 - 1;
+      sofs = (uint32_t)(grp - n0 / 16) * (uint32_t)K + 4u * (lane & 15);
+      slds = kXSOff + wave * 256;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int rl = 64 * wave + 32 * j + (lane >> 1);
+      int r = n0 + rl;
+      r = r < N ? r : N - 1;
+      wofs[j] = (uint32_t)(r - n0) * (uint32_t)(K / 2) + 16u * ((lane & 1) ^ (((rl >> 2) ^ (rl >> 3)) & 1));
+      wlds[j] = kXWOff + (wave * 2 + j) * 1024;
+    }
+    {
+      int r = n0 + 64 * wave + lane;
+      r = r < N ? r : N - 1;
+      sofs = (uint32_t)(r - n0) * (uint32_t)(K / 16);
+      slds = kXSOff + wave * 256;
+    }
   }
   const unsigned char* abase = reinterpret_cast<const unsigned char*>(a16) + (size_t)m0 * K * 2;
   const uint8_t* wbase = w + (size_t)n0 * (K / 2);
@@ -591,9 +627,11 @@ gemm_wide(const _Float16* __restrict__ a16, const float* __restrict__ rowscale,
     const uint32_t l0 = lds_addr(buf);
 #pragma unroll
     for (int j = 0; j < 2; ++j) dma16(ab, aofs[j], l0 + alds[j]);
+    const uint8_t* wst = TILED ? wbase + (size_t)st * 512 : wbase + k0 / 2;
+    const uint8_t* sst = TILED ? sbase + (size_t)st * 64 : sbase + k0 / 16;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) dma16(wbase + k0 / 2, wofs[j], l0 + wlds[j]);
-    dma4(sbase + k0 / 16, sofs, l0 + slds);
+    for (int j = 0; j < 2; ++j) dma16(wst, wofs[j], l0 + wlds[j]);
+    dma4(sst, sofs, l0 + slds);
   };
   constexpr int kLoads = 5;   // per wave per stage
 
@@ -615,8 +653,15 @@ gemm_wide(const _Float16* __restrict__ a16, const float* __restrict__ rowscale,
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int nl = wave * 64 + nt * 32 + l32;
-      wcode[nt] = *reinterpret_cast<const uint4*>(st + kXWOff + nl * 32 + 16 * (h ^ (((nl >> 2) ^ (nl >> 3)) & 1)));
-      const uint32_t sw = *reinterpret_cast<const uint32_t*>(st + kXSOff + nl * 4) >> (16 * h);
+      uint32_t sw;
+      if constexpr (TILED) {
+        const int pos = (nl >> 4) * 32 + (nl & 15) + 16 * h;   // lane order of the row group
+        wcode[nt] = *reinterpret_cast<const uint4*>(st + kXWOff + pos * 16);
+        sw = *reinterpret_cast<const uint16_t*>(st + kXSOff + pos * 2);
+      } else {
+        wcode[nt] = *reinterpret_cast<const uint4*>(st + kXWOff + nl * 32 + 16 * (h ^ (((nl >> 2) ^ (nl >> 3)) & 1)));
+        sw = *reinterpret_cast<const uint32_t*>(st + kXSOff + nl * 4) >> (16 * h);
+      }
       wsc[nt][0] = e4m3_b0_f16(sw);
       wsc[nt][1] = e4m3_b1_f16(sw);
     }
@@ -691,14 +736,38 @@ size_t gemm_workspace_bytes(int64_t B, int64_t N, int64_t K) {
   return align256((size_t)B * (size_t)K * 2) + align256((size_t)B * 4);
 }
 
+// Pre-tiled weight layout (offline, once per weight): row group G = rows
+// 16G .. 16G+15; for each 128-k chunk c a 1 KiB tile of codes whose 16-byte
+// lane l = r + 16 q holds the 32 codes of row 16G + r at k = 128c + 32q ..
+// +31, and a 128-byte tile of E4M3 bytes whose 2-byte lane l holds that
+// row's bytes for the same 32 k.  Tiles are stored (G, c) row-major, so a row
+// group's codes are contiguous (K*8 bytes), as are its E4M3 bytes (K bytes).
+// One thread per lane: a plain permutation of 16-byte and 2-byte pieces.
+__global__ void __launch_bounds__(256)
+pretile_weight(const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_sf, int64_t ntiles,
+               int nch, int K, uint8_t* __restrict__ wt, uint8_t* __restrict__ st) {
+  const int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tile >= ntiles) return;
+  const int l = threadIdx.x & 63;
+  const int64_t grp = tile / nch;
+  const int c = (int)(tile - grp * nch);
+  const int64_t r = 16 * grp + (l & 15);
+  const int k = 128 * c + 32 * (l >> 4);
+  *reinterpret_cast<uint4*>(wt + (tile * 64 + l) * 16) =
+      *reinterpret_cast<const uint4*>(w + r * (K / 2) + k / 2);
+  *reinterpret_cast<uint16_t*>(st + (tile * 64 + l) * 2) =
+      *reinterpret_cast<const uint16_t*>(w_sf + r * (K / 16) + k / 16);
+}
+
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, []() {
-    for (int a4 = 0; a4 < 2 && attr_err == hipSuccess; ++a4)
-      for (int ni = 1; ni <= kSkItems && attr_err == hipSuccess; ni *= 2)
-        attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(skinny_kernel(a4 != 0, ni)),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSkinnyDynMax);
+    for (int tl = 0; tl < 2 && attr_err == hipSuccess; ++tl)
+      for (int a4 = 0; a4 < 2 && attr_err == hipSuccess; ++a4)
+        for (int ni = 1; ni <= kSkItems && attr_err == hipSuccess; ni *= 2)
+          attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(skinny_kernel(a4 != 0, ni, tl != 0)),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSkinnyDynMax);
     if (attr_err == hipSuccess)
       attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTiledLds);
@@ -710,7 +779,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (use_skinny(g.B, g.K)) {
     const unsigned grid = (unsigned)((N + kSkRows - 1) / kSkRows);
     const int ni = B * ((K / 8 + kSkThreads - 1) / kSkThreads);
-    const SkinnyFn fn = skinny_kernel(((uintptr_t)g.a % 4) == 0, ni);
+    const SkinnyFn fn = skinny_kernel(((uintptr_t)g.a % 4) == 0, ni, g.tiled != 0);
     hipLaunchKernelGGL(fn, dim3(grid), dim3(kSkThreads), skinny_lds_bytes(B, K), s, g.a, g.a_scale,
                        g.w, g.w_sf, g.w_g, y, B, N, K);
     return hipGetLastError();
@@ -718,18 +787,32 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   unsigned char* ws = reinterpret_cast<unsigned char*>(g.workspace);
   _Float16* a16 = reinterpret_cast<_Float16*>(ws);
   float* rowscale = reinterpret_cast<float*>(ws + align256((size_t)B * (size_t)K * 2));
+  // gemm_wide's copies take 32-bit lane offsets of up to 512 rows x K bytes
+  const bool wide = g.tiled || (K % kTK == 0 && ((uintptr_t)g.w_sf % 4) == 0 && g.K <= (1 << 24));
   hipLaunchKernelGGL(a_to_f16_rows, dim3((unsigned)B), dim3(256), 0, s, g.a, g.a_scale, a16,
                      rowscale, K);
-  // gemm_wide's copies take 32-bit lane offsets of up to 512 rows x K bytes
-  if (K % kTK == 0 && ((uintptr_t)g.w_sf % 4) == 0 && g.K <= (1 << 24)) {
+  if (wide) {
     const int wtm = (B + kXM - 1) / kXM, wtn = (N + kXN - 1) / kXN;
-    hipLaunchKernelGGL(gemm_wide, dim3((unsigned)(wtm * wtn)), dim3(kP2Threads), 0, s, a16,
-                       rowscale, g.w, g.w_sf, g.w_g, y, B, N, K, wtm, wtn);
+    if (g.tiled)
+      hipLaunchKernelGGL(gemm_wide<true>, dim3((unsigned)(wtm * wtn)), dim3(kP2Threads), 0, s, a16,
+                         rowscale, g.w, g.w_sf, g.w_g, y, B, N, K, wtm, wtn);
+    else
+      hipLaunchKernelGGL(gemm_wide<false>, dim3((unsigned)(wtm * wtn)), dim3(kP2Threads), 0, s, a16,
+                         rowscale, g.w, g.w_sf, g.w_g, y, B, N, K, wtm, wtn);
   } else {
     const int tiles_m = (B + kTM - 1) / kTM, tiles_n = (N + kTN - 1) / kTN;
     hipLaunchKernelGGL(gemm_tiled, dim3((unsigned)(tiles_m * tiles_n)), dim3(kTThreads), kTiledLds,
                        s, a16, rowscale, g.w, g.w_sf, g.w_g, y, B, N, K, tiles_n);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_pretile(const uint8_t* w, const uint8_t* w_sf, int64_t N, int64_t K,
+                          uint8_t* w_tiled, uint8_t* sf_tiled, hipStream_t s) {
+  const int nch = (int)(K / 128);
+  const int64_t ntiles = N / 16 * nch;
+  hipLaunchKernelGGL(pretile_weight, dim3((unsigned)((ntiles + 3) / 4)), dim3(256), 0, s, w, w_sf, ntiles,
+                     nch, (int)K, w_tiled, sf_tiled);
   return hipGetLastError();
 }
 

@@ -42,9 +42,12 @@ struct GemmArgs {
   int64_t B, N, K;
   void* workspace;
   size_t workspace_bytes;
+  int tiled;           // w / w_sf in the pre-tiled layout (N % 16 == 0, K % 128 == 0)
 };
 
 size_t gemm_workspace_bytes(int64_t B, int64_t N, int64_t K);
+hipError_t launch_pretile(const uint8_t* w, const uint8_t* w_sf, int64_t N, int64_t K,
+                          uint8_t* w_tiled, uint8_t* sf_tiled, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
 
 struct MoeArgs {

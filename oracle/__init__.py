@@ -290,3 +290,38 @@ def moe_ref(x_fp16: np.ndarray, ids: np.ndarray, weights: np.ndarray,
         for j in range(top_k):
             out[oi] += float(weights[t, j]) * o[(t, j)]
     return out
+
+
+# ---------------------------------------------------------------- pre-tiled weights
+# The layout is a pure reordering defined in include/nvfp4_mi355x.h (the role
+# of the baked N128_K64 weight tiling of "Nvfp4 A16 Blackwell Moe Runner" and
+# of the weight shuffles of "feature: add fp4 mm using trtllm backend"):
+# row group G = rows 16G..16G+15, 128-k chunk c, 16-byte lane l = r + 16q
+# holds the 32 codes of row 16G + r at k = 128c + 32q .. +31; the 2-byte
+# scale lane l holds that row's two E4M3 bytes for the same k.
+
+def pretile_weight_loops(w_codes: np.ndarray, w_sf: np.ndarray):
+    """The layout written out element by element (small sizes only)."""
+    N, K = w_codes.shape[0], w_codes.shape[1] * 2
+    nch = K // 128
+    wt = np.zeros(N * K // 2, np.uint8)
+    st = np.zeros(N * K // 16, np.uint8)
+    for G in range(N // 16):
+        for c in range(nch):
+            for lane in range(64):
+                r, q = 16 * G + lane % 16, lane // 16
+                k = 128 * c + 32 * q
+                t = (G * nch + c) * 64 + lane
+                wt[16 * t:16 * t + 16] = w_codes[r, k // 2:k // 2 + 16]
+                st[2 * t:2 * t + 2] = w_sf[r, k // 16:k // 16 + 2]
+    return wt, st
+
+
+def pretile_weight(w_codes: np.ndarray, w_sf: np.ndarray):
+    """Same layout by reshaping: codes [G, r, c, q, 16 B] -> [G, c, q, r, 16 B],
+    E4M3 bytes [G, r, c, q, 2 B] -> [G, c, q, r, 2 B]."""
+    N, K = w_codes.shape[0], w_codes.shape[1] * 2
+    nch = K // 128
+    wt = w_codes.reshape(N // 16, 16, nch, 4, 16).transpose(0, 2, 3, 1, 4).reshape(-1)
+    st = w_sf.reshape(N // 16, 16, nch, 4, 2).transpose(0, 2, 3, 1, 4).reshape(-1)
+    return np.ascontiguousarray(wt), np.ascontiguousarray(st)

@@ -106,3 +106,16 @@ def test_external_weight_registry_without_gpu(nv):
     assert L.nvfp4_unregister_weight(0, 8) == nv.NVFP4_EINVAL
     p = ctypes.c_void_p(256)
     assert L.nvfp4_gemm_external(p, p, -3, p, p, 4, 64, 128, None, 0, None) == nv.NVFP4_EINVAL
+
+
+def test_pretiled_validation_without_gpu(nv):
+    L = nv.lib()
+    p, p4 = ctypes.c_void_p(4096), ctypes.c_void_p(4100)
+    # N % 16, K % 128, alignment of the tiled scale buffer
+    assert L.nvfp4_pretile_weight(p, p, 40, 256, p, p, None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_pretile_weight(p, p, 48, 320, p, p, None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_pretile_weight(p, p, 48, 256, p, ctypes.c_void_p(4098), None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_gemm_pretiled(p, p, p, p, p, p, 4, 40, 256, None, 0, None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_gemm_pretiled(p, p, p, p, p, p, 4, 48, 192, None, 0, None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_gemm_pretiled(p, p, ctypes.c_void_p(4104), p, p, p, 4, 48, 256, None, 0, None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_gemm_pretiled(p, p4, p, p, p, p, 0, 48, 256, None, 0, None) == nv.NVFP4_OK   # B == 0

@@ -157,3 +157,32 @@ def test_prefill_path_past_4gib_of_fp16_activations(nv, oracle):
     assert oracle.rel_fro(got, ref) <= TOL
     del t, y
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("N,K", [(16, 128), (48, 384), (8192, 4096)])
+def test_pretile_matches_oracle(nv, oracle, N, K):
+    d = si.random_nvfp4_operands(1, N, K, seed=N + K)
+    dev = "cuda"
+    t = nv.pretile_weight(torch.from_numpy(d["w_codes"]).to(dev), torch.from_numpy(d["w_sf"]).to(dev))
+    torch.cuda.synchronize()
+    wt, st = oracle.pretile_weight(d["w_codes"], d["w_sf"])
+    assert np.array_equal(t["codes"].cpu().numpy(), wt)
+    assert np.array_equal(t["sf"].cpu().numpy(), st)
+
+
+@pytest.mark.parametrize("B,N,K", [(1, 8192, 4096), (4, 48, 384), (16, 64, 256), (17, 48, 384),
+                                   (300, 528, 640), (64, 512, 1024)])
+def test_gemm_pretiled_matches_untiled(nv, oracle, B, N, K):
+    # decode (B <= 16) and prefill kernels on the pre-tiled layout: the same
+    # products in the same order as on [N, K/2] weights -> bit-identical
+    d = si.random_nvfp4_operands(B, N, K, seed=B * 7 + N + K)
+    dev = "cuda"
+    t = {k: torch.from_numpy(v).to(dev) for k, v in d.items()}
+    y0 = nv.gemm(t["a_codes"], t["a_scale"], t["w_codes"], t["w_sf"], t["w_g"])
+    wt = nv.pretile_weight(t["w_codes"], t["w_sf"])
+    y1 = nv.gemm_pretiled(t["a_codes"], t["a_scale"], wt, t["w_g"])
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    ref = oracle.gemm_ref(d["a_codes"], d["a_scale"], d["w_codes"], d["w_sf"], d["w_g"][0],
+                          rows=list(range(min(B, 8))))
+    assert oracle.rel_fro(y1[:min(B, 8)].cpu().double().numpy(), ref) <= TOL

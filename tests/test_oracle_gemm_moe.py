@@ -174,3 +174,36 @@ def test_moe_ref_closed_form(oracle):
     g1 = np.full(E, 2.0, np.float32); g2 = np.full(E, 3.0, np.float32)
     out2 = oracle.moe_ref(x.numpy(), ids, wts, w1c, w1s, g1, w1c, w1s, g2)
     assert np.allclose(out2, xr * 4.0 * 3.0, rtol=1e-14)
+
+
+# ---------------------------------------------------------------- pre-tiled weights
+
+def test_pretile_worked_positions(oracle):
+    # distinct byte values make each position unambiguous: code byte j of
+    # row r is (r * 64 + j) % 251, scale byte j of row r is (r * 8 + j) % 127
+    N, K = 32, 256
+    w = np.fromfunction(lambda r, j: (r * 64 + j) % 251, (N, K // 2)).astype(np.uint8)
+    s = np.fromfunction(lambda r, j: (r * 8 + j) % 127, (N, K // 16)).astype(np.uint8)
+    wt, st = oracle.pretile_weight(w, s)
+    tile = lambda G, c, lane: (G * (K // 128) + c) * 64 + lane
+    # group 0, chunk 0, lane 17 = row 1, k 32..63 -> code bytes 16..31, scale bytes 2, 3
+    assert wt[16 * 17:16 * 18].tolist() == w[1, 16:32].tolist()
+    assert st[2 * 17:2 * 18].tolist() == s[1, 2:4].tolist()
+    # group 1, chunk 1, lane 63 = row 31, k = 128 + 96 .. 255 -> code bytes 112..127, scale 14, 15
+    t = tile(1, 1, 63)
+    assert wt[16 * t:16 * t + 16].tolist() == w[31, 112:128].tolist()
+    assert st[2 * t:2 * t + 2].tolist() == s[31, 14:16].tolist()
+    # a row group is contiguous: group 1 starts at 16 rows * K/2 bytes
+    assert wt[16 * tile(1, 0, 0):16 * tile(1, 0, 0) + 16].tolist() == w[16, 0:16].tolist()
+
+
+def test_pretile_reshape_matches_loops_and_is_a_permutation(oracle):
+    rng = np.random.default_rng(12)
+    for N, K in [(16, 128), (48, 384), (32, 1024)]:
+        w = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+        s = rng.integers(0, 127, (N, K // 16), dtype=np.uint8)
+        wt, st = oracle.pretile_weight(w, s)
+        wl, sl = oracle.pretile_weight_loops(w, s)
+        assert np.array_equal(wt, wl) and np.array_equal(st, sl)
+        assert np.array_equal(np.sort(wt), np.sort(w.reshape(-1)))
+        assert np.array_equal(np.sort(st), np.sort(s.reshape(-1)))
