@@ -74,6 +74,12 @@ def lib() -> ctypes.CDLL:
         L.oracle_activation.restype = c_i
         L.oracle_route.argtypes = [c_p, c_p, c_i, c_i, c_i, c_i, c_i, c_i, c_f, c_p, c_p]
         L.oracle_route.restype = c_i
+        L.oracle_e8m0_decode.argtypes = [c_u8]; L.oracle_e8m0_decode.restype = c_d
+        L.oracle_e8m0_encode_up.argtypes = [c_f]; L.oracle_e8m0_encode_up.restype = c_u8
+        L.oracle_mx_quantize_block.argtypes = [c_p, c_f, c_f, c_p, c_p, c_p]
+        L.oracle_mx_quantize_block.restype = None
+        L.oracle_mx_quantize.argtypes = [c_p, c_i, c_i64, c_i64, c_i, c_i64, c_p, c_p, c_p]
+        L.oracle_mx_quantize.restype = c_i
         _lib = L
     return _lib
 
@@ -325,3 +331,112 @@ def pretile_weight(w_codes: np.ndarray, w_sf: np.ndarray):
     wt = w_codes.reshape(N // 16, 16, nch, 4, 16).transpose(0, 2, 3, 1, 4).reshape(-1)
     st = w_sf.reshape(N // 16, 16, nch, 4, 2).transpose(0, 2, 3, 1, 4).reshape(-1)
     return np.ascontiguousarray(wt), np.ascontiguousarray(st)
+
+
+# ---------------------------------------------------------------- MXFP4 variant
+# The UE8M0_SF switch of the block helper in "perf: optimize per-token nvfp4
+# quantization kernel" (review): E8M0 block scales over 32 elements.  The
+# readings are listed at the top of nvfp4_oracle.c.
+
+def e8m0_decode(b: int) -> float:
+    return lib().oracle_e8m0_decode(int(b))
+
+
+def e8m0_encode_up(x: float) -> int:
+    return lib().oracle_e8m0_encode_up(float(x))
+
+
+def mx_quantize_block(y32: np.ndarray, g_enc: float, g_dec: float):
+    """One 32-element block -> (E8M0 byte, combined fp32 scale, 16 code bytes)."""
+    y = np.ascontiguousarray(y32, dtype=np.float32)
+    assert y.shape == (32,)
+    sf = ctypes.c_uint8(); c = ctypes.c_float(); codes = np.zeros(16, np.uint8)
+    lib().oracle_mx_quantize_block(_ptr(y), float(g_enc), float(g_dec), ctypes.byref(sf),
+                                   ctypes.byref(c), _ptr(codes))
+    return sf.value, c.value, codes
+
+
+def mx_quantize(x, act: int = ACT_NONE, group_rows: int = 1):
+    """MXFP4-quantize a 2-D bf16/fp16 tensor.
+
+    Returns dict(codes [rows, k/2] u8, sf [rows, k/32] u8 E8M0, g_dec [rows/group_rows] f32).
+    """
+    u16, dt = _as_u16(x)
+    rows, k_in = u16.shape
+    k_out = k_in // 2 if act == ACT_SWIGLU else k_in
+    codes = np.zeros((rows, k_out // 2), np.uint8)
+    sf = np.zeros((rows, k_out // 32), np.uint8)
+    g = np.zeros((rows // group_rows if rows else 0,), np.float32)
+    rc = lib().oracle_mx_quantize(_ptr(u16), dt, rows, k_in, act, group_rows, _ptr(codes),
+                                  _ptr(sf), _ptr(g))
+    if rc != 0:
+        raise ValueError("oracle_mx_quantize rejected the arguments")
+    return {"codes": codes, "sf": sf, "g_dec": g}
+
+
+def e8m0_table() -> np.ndarray:
+    return np.array([e8m0_decode(b) for b in range(256)], np.float64)
+
+
+def dequant_mx(codes: np.ndarray, sf: np.ndarray, g_dec) -> np.ndarray:
+    """e2m1(code) * e8m0(block scale) * fp32 global scale (one per row, or a scalar)."""
+    q = _E2M1[unpack_codes(codes)]
+    g = np.asarray(g_dec, np.float32).astype(np.float64)
+    if g.ndim == 1:
+        g = g[:, None]
+    return q * np.repeat(e8m0_table()[sf], 32, axis=-1) * g
+
+
+def mx_gemm_ref(a_codes, a_sf, a_g, w_codes, w_sf, w_g, rows=None) -> np.ndarray:
+    """y[B, N] = deq(a) . deq(w)^T in float64; a_g one global per row, w_g a scalar."""
+    if rows is not None:
+        a_codes, a_sf, a_g = a_codes[rows], a_sf[rows], np.asarray(a_g)[rows]
+    A = dequant_mx(a_codes, a_sf, a_g)
+    W = dequant_mx(w_codes, w_sf, np.float32(w_g))
+    return A @ W.T
+
+
+# The MX tile layout (defined in include/nvfp4_mi355x.h): rows padded to a
+# multiple of 32 with zero codes and zero scale bytes; row group G = rows
+# 32G..32G+31; per 64-k chunk a 1 KiB code tile whose 16-byte lane
+# l = r + 32h holds the codes of row 32G + r at k = 64c + 32h .. +31; per
+# 128-k chunk a 128 B scale tile whose 2-byte lane l = r + 32h holds, in byte j,
+# the E8M0 byte of block 4c + 2j + h of row 32G + r.  Tiles are stored
+# (G, chunk) row-major.
+
+def mx_tile_loops(codes: np.ndarray, sf: np.ndarray):
+    """The layout written out element by element (small sizes only)."""
+    R, K = codes.shape[0], codes.shape[1] * 2
+    G = (R + 31) // 32
+    ct = np.zeros(G * 32 * K // 2, np.uint8)
+    st = np.zeros(G * 32 * K // 32, np.uint8)
+    for g in range(G):
+        for c in range(K // 64):
+            for lane in range(64):
+                r, h = 32 * g + lane % 32, lane // 32
+                if r >= R:
+                    continue
+                k = 64 * c + 32 * h
+                t = (g * (K // 64) + c) * 64 + lane
+                ct[16 * t:16 * t + 16] = codes[r, k // 2:k // 2 + 16]
+        for c in range(K // 128):
+            for lane in range(64):
+                r, h = 32 * g + lane % 32, lane // 32
+                if r >= R:
+                    continue
+                t = (g * (K // 128) + c) * 64 + lane
+                for j in range(2):
+                    st[2 * t + j] = sf[r, 4 * c + 2 * j + h]
+    return ct, st
+
+
+def mx_tile(codes: np.ndarray, sf: np.ndarray):
+    """Same layout by reshaping: codes [G, r, c, h, 16 B] -> [G, c, h, r, 16 B];
+    scale bytes [G, r, c, j, h] -> [G, c, h, r, j]."""
+    R, K = codes.shape[0], codes.shape[1] * 2
+    G = (R + 31) // 32
+    cp = np.zeros((G * 32, K // 2), np.uint8); cp[:R] = codes
+    sp = np.zeros((G * 32, K // 32), np.uint8); sp[:R] = sf
+    ct = cp.reshape(G, 32, K // 64, 2, 16).transpose(0, 2, 3, 1, 4).reshape(-1)
+    st = sp.reshape(G, 32, K // 128, 2, 2).transpose(0, 2, 4, 1, 3).reshape(-1)
+    return np.ascontiguousarray(ct), np.ascontiguousarray(st)

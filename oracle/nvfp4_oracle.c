@@ -37,6 +37,13 @@
  *  - SwiGLU: gate = first half of the row, up = second half;
  *    y = (g / (1 + exp(-g))) * u with the exp defined by oracle_exp below.
  *  - ReLU2: y = r*r with r = max(x, +0).
+ *  - MXFP4 variant (the UE8M0_SF switch of the block helper in [P4], review;
+ *    the pages show only the switch): 32-element blocks; the same global
+ *    scale and block amax as above; the block scale is an E8M0 byte (value
+ *    2^(b-127)), namely the smallest such power of two >= (amax_b / 6) * g_enc,
+ *    so no element of a block saturates; at or above 2^127 (and for NaN) it
+ *    is byte 254, at or below 2^-127 byte 0; c = e8m0(b) * g_dec, enc = 1/c,
+ *    elements as above.
  * All float arithmetic is IEEE-754 binary32, round-to-nearest-even, one
  * rounding per operation, no contraction (build with -ffp-contract=off);
  * fmaf is used only where an fma is written explicitly.
@@ -371,5 +378,77 @@ int oracle_route(const float* logits, const float* bias, int tokens, int experts
       weights[(int64_t)t * top_k + k] = weights[(int64_t)t * top_k + k] * routed_scaling;
   }
   free(s); free(b); free(gs); free(keep); free(used);
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* MXFP4 variant: E8M0 block scales over 32 elements ([P4] review, the  */
+/* UE8M0_SF switch of the block helper; readings in the header).        */
+/* ------------------------------------------------------------------ */
+
+/* E8M0: byte b is 2^(b - 127); 255 is NaN and never produced here. */
+double oracle_e8m0_decode(uint8_t b) {
+  if (b == 255) return NAN;
+  return ldexp(1.0, (int)b - 127);
+}
+
+/* Smallest E8M0 value >= x, by search over the 255 finite codes (the values
+ * increase with the code).  x above 2^127 or NaN gives 254. */
+uint8_t oracle_e8m0_encode_up(float x) {
+  double xv = (double)x;
+  if (!(xv <= ldexp(1.0, 127))) return 254;
+  for (int b = 0; b <= 254; ++b)
+    if (oracle_e8m0_decode((uint8_t)b) >= xv) return (uint8_t)b;
+  return 254;
+}
+
+/* One 32-element block: E8M0 byte, combined scale c, 16 packed code bytes. */
+void oracle_mx_quantize_block(const float* y, float g_enc, float g_dec, uint8_t* sf_out,
+                              float* c_out, uint8_t* codes16) {
+  float amax_b = 0.0f;
+  for (int i = 0; i < 32; ++i) amax_b = fmaxf(amax_b, fabsf(y[i]));
+  float sf_f = (amax_b / 6.0f) * g_enc;
+  uint8_t sf = oracle_e8m0_encode_up(sf_f);
+  float c = (float)oracle_e8m0_decode(sf) * g_dec;   /* one binary32 rounding */
+  float enc = (c == 0.0f) ? 0.0f : 1.0f / c;
+  for (int i = 0; i < 16; ++i) {
+    float v0 = (y[2 * i] == 0.0f) ? y[2 * i] : y[2 * i] * enc;
+    float v1 = (y[2 * i + 1] == 0.0f) ? y[2 * i + 1] : y[2 * i + 1] * enc;
+    codes16[i] = (uint8_t)(oracle_e2m1_encode(v0) | (oracle_e2m1_encode(v1) << 4));
+  }
+  *sf_out = sf;
+  *c_out = c;
+}
+
+/*
+ * Same arguments as oracle_quantize, with 32-element blocks:
+ * codes [rows, k_out/2], sf [rows, k_out/32] E8M0 bytes, g_dec [rows/group_rows].
+ */
+int oracle_mx_quantize(const uint16_t* x, int dtype, int64_t rows, int64_t k_in, int act,
+                       int64_t group_rows, uint8_t* codes, uint8_t* sf, float* g_dec) {
+  if (rows < 0 || k_in <= 0 || group_rows <= 0 || (rows % group_rows) != 0) return -1;
+  int64_t k_out = (act == ACT_SWIGLU) ? k_in / 2 : k_in;
+  if ((act == ACT_SWIGLU && (k_in % 2) != 0) || (k_out % 32) != 0) return -1;
+  int64_t nb = k_out / 32;
+  float* y = (float*)malloc(sizeof(float) * (size_t)k_out);
+  if (!y) return -1;
+  for (int64_t g0 = 0; g0 < rows; g0 += group_rows) {
+    float amax = 0.0f;
+    for (int64_t r = g0; r < g0 + group_rows; ++r)
+      for (int64_t j = 0; j < k_out; ++j)
+        amax = fmaxf(amax, fabsf(act_value(x, dtype, k_in, act, r, j, k_out)));
+    float g_enc, gd;
+    oracle_global_scale(amax, &g_enc, &gd);
+    g_dec[g0 / group_rows] = gd;
+    for (int64_t r = g0; r < g0 + group_rows; ++r) {
+      for (int64_t j = 0; j < k_out; ++j) y[j] = act_value(x, dtype, k_in, act, r, j, k_out);
+      for (int64_t b = 0; b < nb; ++b) {
+        float cb;
+        oracle_mx_quantize_block(y + 32 * b, g_enc, gd, sf + r * nb + b, &cb,
+                                 codes + r * (k_out / 2) + 16 * b);
+      }
+    }
+  }
+  free(y);
   return 0;
 }
