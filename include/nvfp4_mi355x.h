@@ -233,6 +233,71 @@ int32_t nvfp4_moe_w4a16(const float* router_logits, const float* correction_bias
 size_t nvfp4_moe_w4a16_workspace_size(int32_t tokens, int32_t experts, int32_t top_k, int32_t hidden,
                                       int32_t inter);
 
+/*
+ * MXFP4 variant -- the UE8M0_SF switch of the block helper in "perf: optimize
+ * per-token nvfp4 quantization kernel" (review): 32-element K-blocks whose
+ * scale is one E8M0 byte b (value 2^(b-127)), the format gfx950's block-scaled
+ * MFMA consumes directly.  Arithmetic as for NVFP4 (same global scale per
+ * group of rows), except per block:
+ *   sf = smallest power of two >= (amax_b / 6) * g_enc, saturating at 2^127
+ *        (byte 254; also for NaN), at least 2^-127 (byte 0)
+ *   c  = sf * g_dec,  enc = (c == 0) ? 0 : 1 / c,  code = E2M1_RNE_sat(y * enc)
+ * so no element of a block saturates.  Dequantization: e2m1(code) * 2^(b-127)
+ * * g_dec.
+ *
+ * MX tile layout (the operand order of the MFMA's lanes), for an operand of
+ * R rows and K columns (K % 128 == 0): rows padded to R32 = 32*ceil(R/32);
+ * row group G = rows 32G..32G+31.
+ *   codes : per (G, 64-k chunk c) a 1 KiB tile; its 16-byte lane l = r + 32h
+ *           (r < 32, h < 2) holds the 32 codes of row 32G + r at k = 64c + 32h
+ *           .. +31, packed as in [R, K/2].  [R32/32][K/64][64][16 B] = R32*K/2 bytes.
+ *   scales: per (G, 128-k chunk c) a 128-byte tile; its 2-byte lane l = r + 32h
+ *           holds in byte j the E8M0 byte of block 4c + 2j + h of row 32G + r.
+ *           [R32/32][K/128][64][2 B] = R32*K/32 bytes.
+ * Padding rows hold zero codes and zero scale bytes.
+ */
+#define NVFP4_MX_ROWS 0    /* codes [rows, k/2], E8M0 bytes [rows, k/32] */
+#define NVFP4_MX_TILED 1   /* the MX tile layout */
+
+/*
+ * nvfp4_mx_quantize -- MXFP4 quantization of x with the optional activation
+ * of nvfp4_act_quant in front (act != NONE needs group_rows == 1).
+ *   x         : [rows, k_in] bf16 or fp16, 16-byte aligned (k_in = 2*k for SWIGLU)
+ *   layout    : NVFP4_MX_ROWS (k % 32 == 0) or NVFP4_MX_TILED (k % 128 == 0;
+ *               codes R32*k/2 bytes, sf R32*k/32 bytes, padding rows written)
+ *   codes, sf : outputs in that layout; codes 4-byte aligned
+ *   g_dec     : [rows / group_rows] float out
+ *   workspace : nvfp4_quantize_workspace_size(rows, k, group_rows) bytes
+ * Requires k <= 32768 (the row is held in registers), rows % group_rows == 0.
+ */
+int32_t nvfp4_mx_quantize(const void* x, int32_t dtype, int64_t rows, int64_t k, int32_t act,
+                          int64_t group_rows, int32_t layout, uint8_t* codes, uint8_t* sf,
+                          float* g_dec, void* workspace, size_t workspace_bytes, void* stream);
+/*
+ * nvfp4_mx_tile -- writes the MX tile layout from [rows, k/2] codes and
+ * [rows, k/32] E8M0 bytes (a permutation; padding rows zero).  Offline for
+ * weights.  Requires k % 128 == 0, k <= 2^24; codes and codes_tiled 16-byte,
+ * sf_tiled 2-byte aligned.
+ */
+int32_t nvfp4_mx_tile(const uint8_t* codes, const uint8_t* sf, int64_t rows, int64_t k,
+                      uint8_t* codes_tiled, uint8_t* sf_tiled, void* stream);
+/*
+ * nvfp4_mx_gemm -- y[B,N] (fp16) = sum_k deq(a)[B,k] * deq(w)[N,k] for MXFP4
+ * operands in the MX tile layout, on v_mfma_scale_f32_32x32x64_f8f6f4 (FP4 x
+ * FP4 with the E8M0 bytes as the instruction's block scales; fp32
+ * accumulation; y = fp16_RNE(acc * (a_g[row / a_group_rows] * w_gscale[0]))).
+ *   a_tiled, a_sf_tiled : activation tiles (B rows), e.g. from nvfp4_mx_quantize
+ *   a_g                 : [B / a_group_rows] float activation globals (1 = per token)
+ *   w_tiled, w_sf_tiled : weight tiles (N rows), e.g. from nvfp4_mx_tile
+ *   w_gscale            : one device float
+ *   y                   : [B, N] fp16, 8-byte aligned
+ * Requires N % 32 == 0, K % 128 == 0, K <= 2^24, B % a_group_rows == 0;
+ * tiles 16-byte and scale tiles, a_g, w_gscale 4-byte aligned.  B == 0 is a no-op.
+ */
+int32_t nvfp4_mx_gemm(const uint8_t* a_tiled, const uint8_t* a_sf_tiled, const float* a_g,
+                      int64_t a_group_rows, const uint8_t* w_tiled, const uint8_t* w_sf_tiled,
+                      const float* w_gscale, void* y, int64_t B, int64_t N, int64_t K, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

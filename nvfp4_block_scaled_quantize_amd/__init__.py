@@ -23,8 +23,10 @@ EXPORTS = [
     "nvfp4_status_string", "nvfp4_quantize", "nvfp4_quantize_workspace_size", "nvfp4_act_quant",
     "nvfp4_gemm", "nvfp4_gemm_workspace_size", "nvfp4_moe_w4a16", "nvfp4_moe_w4a16_workspace_size",
     "nvfp4_register_weight", "nvfp4_unregister_weight", "nvfp4_gemm_external",
-    "nvfp4_pretile_weight", "nvfp4_gemm_pretiled",
+    "nvfp4_pretile_weight", "nvfp4_gemm_pretiled", "nvfp4_mx_quantize", "nvfp4_mx_tile",
+    "nvfp4_mx_gemm",
 ]
+MX_ROWS, MX_TILED = 0, 1
 
 
 class Nvfp4Error(RuntimeError):
@@ -66,6 +68,12 @@ def _load() -> ctypes.CDLL:
     L.nvfp4_pretile_weight.restype = i32
     L.nvfp4_gemm_pretiled.argtypes = [p, p, p, p, p, p, i64, i64, i64, p, sz, p]
     L.nvfp4_gemm_pretiled.restype = i32
+    L.nvfp4_mx_quantize.argtypes = [p, i32, i64, i64, i32, i64, i32, p, p, p, p, sz, p]
+    L.nvfp4_mx_quantize.restype = i32
+    L.nvfp4_mx_tile.argtypes = [p, p, i64, i64, p, p, p]
+    L.nvfp4_mx_tile.restype = i32
+    L.nvfp4_mx_gemm.argtypes = [p, p, p, i64, p, p, p, p, i64, i64, i64, p]
+    L.nvfp4_mx_gemm.restype = i32
     return L
 
 
@@ -269,3 +277,77 @@ def moe_w4a16(logits, bias, x, w1, w1_sf, w1_g, w2, w2_sf, w2_g, top_k, n_group,
     if st != NVFP4_OK:
         raise Nvfp4Error(st, "nvfp4_moe_w4a16")
     return (o, ids, wts) if want_routing else o
+
+
+# ---------------------------------------------------------------- MXFP4 variant
+
+def mx_tiled_sizes(rows: int, k: int) -> tuple[int, int]:
+    """Bytes of the MX tile layout of a [rows, k] operand: (codes, scale bytes)."""
+    r32 = (rows + 31) // 32 * 32
+    return r32 * k // 2, r32 * k // 32
+
+
+def mx_quantize(x: torch.Tensor, act: str = "none", group_rows: int = 1, tiled: bool = False,
+                out: dict | None = None, workspace: torch.Tensor | None = None, stream=None) -> dict:
+    """MXFP4 quantization (E8M0 scale per 32 elements) of x [rows, k_in], with the
+    optional activation in front.  Returns dict(codes, sf, g_dec, rows, K, tiled):
+    [rows, k/2] and [rows, k/32] uint8 in the row layout, flat uint8 tensors in
+    the MX tile layout."""
+    _check_dev(x)
+    rows, k_in = x.shape
+    a = ACT[act] if isinstance(act, str) else int(act)
+    k = k_in // 2 if a == ACT["swiglu"] else k_in
+    dev = x.device
+    if out is None:
+        if tiled:
+            nc, ns = mx_tiled_sizes(rows, k)
+            codes = torch.empty(nc, dtype=torch.uint8, device=dev)
+            sf = torch.empty(ns, dtype=torch.uint8, device=dev)
+        else:
+            codes = torch.empty((rows, k // 2), dtype=torch.uint8, device=dev)
+            sf = torch.empty((rows, k // 32), dtype=torch.uint8, device=dev)
+        out = {"codes": codes, "sf": sf,
+               "g_dec": torch.empty((rows // max(group_rows, 1),), dtype=torch.float32, device=dev)}
+    out.update(rows=rows, K=k, tiled=bool(tiled))
+    ws, wsb = _workspace(_lib.nvfp4_quantize_workspace_size(rows, k, group_rows), dev, workspace)
+    st = _lib.nvfp4_mx_quantize(_ptr(x), _dtype_code(x), rows, k, a, group_rows,
+                                MX_TILED if tiled else MX_ROWS, _ptr(out["codes"]), _ptr(out["sf"]),
+                                _ptr(out["g_dec"]), _ptr(ws), wsb, _stream(stream))
+    if st != NVFP4_OK:
+        raise Nvfp4Error(st, "nvfp4_mx_quantize")
+    return out
+
+
+def mx_tile(codes: torch.Tensor, sf: torch.Tensor, stream=None) -> dict:
+    """The MX tile layout of [rows, k/2] codes and [rows, k/32] E8M0 bytes."""
+    _check_dev(codes, sf)
+    rows, k = codes.shape[0], codes.shape[1] * 2
+    if sf.shape != (rows, k // 32) or codes.dtype != torch.uint8 or sf.dtype != torch.uint8:
+        raise ValueError("codes [rows, k/2] and E8M0 bytes [rows, k/32] expected")
+    nc, ns = mx_tiled_sizes(rows, k)
+    ct = torch.empty(nc, dtype=torch.uint8, device=codes.device)
+    stt = torch.empty(ns, dtype=torch.uint8, device=codes.device)
+    rc = _lib.nvfp4_mx_tile(_ptr(codes), _ptr(sf), rows, k, _ptr(ct), _ptr(stt), _stream(stream))
+    if rc != NVFP4_OK:
+        raise Nvfp4Error(rc, "nvfp4_mx_tile")
+    return {"codes": ct, "sf": stt, "rows": rows, "K": k, "tiled": True}
+
+
+def mx_gemm(a: dict, a_g: torch.Tensor, w: dict, w_g: torch.Tensor, a_group_rows: int = 1,
+            out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y[B, N] fp16 = deq(a) . deq(w)^T for MXFP4 operands in the MX tile layout
+    (dicts from mx_quantize(tiled=True) or mx_tile)."""
+    if not (a.get("tiled") and w.get("tiled")):
+        raise ValueError("mx_gemm takes operands in the MX tile layout")
+    _check_dev(a["codes"], a["sf"], a_g, w["codes"], w["sf"], w_g)
+    B, N, K = a["rows"], w["rows"], a["K"]
+    if w["K"] != K:
+        raise ValueError("operand K differs")
+    if a_g.dtype != torch.float32 or w_g.dtype != torch.float32:
+        raise TypeError("globals must be float32")
+    y = out if out is not None else torch.empty((B, N), dtype=torch.float16, device=a["codes"].device)
+    rc = _lib.nvfp4_mx_gemm(_ptr(a["codes"]), _ptr(a["sf"]), _ptr(a_g), a_group_rows, _ptr(w["codes"]),
+                            _ptr(w["sf"]), _ptr(w_g), _ptr(y), B, N, K, _stream(stream))
+    if rc != NVFP4_OK:
+        raise Nvfp4Error(rc, "nvfp4_mx_gemm")
+    return y

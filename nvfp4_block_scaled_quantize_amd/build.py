@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libnvfp4_mi355x.so")
-SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "moe.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "moe.hip", "mx_gemm.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -126,6 +126,71 @@ int32_t nvfp4_quantize(const void* x, int32_t dtype, int64_t rows, int64_t k, in
                          scale_out, workspace, workspace_bytes, stream);
 }
 
+int32_t nvfp4_mx_quantize(const void* x, int32_t dtype, int64_t rows, int64_t k_out, int32_t act,
+                          int64_t group_rows, int32_t layout, uint8_t* codes, uint8_t* sf,
+                          float* g_dec, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != NVFP4_BF16 && dtype != NVFP4_FP16) return NVFP4_EINVAL;
+  if (act != NVFP4_ACT_NONE && act != NVFP4_ACT_SWIGLU && act != NVFP4_ACT_RELU2) return NVFP4_EINVAL;
+  if (layout != NVFP4_MX_ROWS && layout != NVFP4_MX_TILED) return NVFP4_EINVAL;
+  if (rows < 0 || k_out <= 0 || group_rows < 1) return NVFP4_EINVAL;
+  if ((k_out % (layout == NVFP4_MX_TILED ? 128 : 32)) != 0) return NVFP4_EINVAL;
+  if (act != NVFP4_ACT_NONE && group_rows != 1) return NVFP4_EINVAL;
+  if (rows > 0 && (rows % group_rows) != 0) return NVFP4_EINVAL;
+  if (rows == 0) return NVFP4_OK;
+  if (!x || !codes || !sf || !g_dec) return NVFP4_EINVAL;
+  if (((uintptr_t)x % 16) != 0 || !aligned4(codes) || !aligned4(g_dec)) return NVFP4_EINVAL;
+  if (k_out > 32768 || rows > 0x7FFFFFE0LL) return NVFP4_EUNSUPPORTED;
+  nvfp4::QuantArgs a{};
+  a.x = x; a.dtype = dtype; a.act = act; a.rows = rows; a.k_out = k_out; a.group_rows = group_rows;
+  a.codes = codes; a.sf = sf; a.g_dec = g_dec; a.scale_out = nullptr; a.parts = nullptr;
+  a.nparts = 0; a.mx = 1; a.tiled = (layout == NVFP4_MX_TILED) ? 1 : 0;
+  if (group_rows > 1) {
+    if ((rows / group_rows) > 65535) return NVFP4_EUNSUPPORTED;   // grid.y limit of the partial pass
+    const size_t need = nvfp4_quantize_workspace_size(rows, k_out, group_rows);
+    if (!workspace || workspace_bytes < need || !aligned4(workspace)) return NVFP4_EWORKSPACE;
+    a.parts = (float*)workspace;
+    a.nparts = nvfp4::quant_num_parts(group_rows * k_out);
+  }
+  const int32_t ds = device_status();
+  if (ds != NVFP4_OK) return ds;
+  a.num_cus = current_device()->num_cus;
+  return hip_status(nvfp4::launch_quantize(a, (hipStream_t)stream));
+}
+
+int32_t nvfp4_mx_tile(const uint8_t* codes, const uint8_t* sf, int64_t rows, int64_t k,
+                      uint8_t* codes_tiled, uint8_t* sf_tiled, void* stream) {
+  if (rows < 0 || k <= 0 || (k % 128) != 0) return NVFP4_EINVAL;
+  if (rows == 0) return NVFP4_OK;
+  if (!codes || !sf || !codes_tiled || !sf_tiled) return NVFP4_EINVAL;
+  if (((uintptr_t)codes % 16) != 0 || ((uintptr_t)codes_tiled % 16) != 0 ||
+      ((uintptr_t)sf_tiled % 2) != 0)
+    return NVFP4_EINVAL;
+  if (k > (1LL << 24) || (rows + 31) / 32 * (k / 64) > (1LL << 33)) return NVFP4_EUNSUPPORTED;
+  const int32_t ds = device_status();
+  if (ds != NVFP4_OK) return ds;
+  return hip_status(nvfp4::launch_mx_tile(codes, sf, rows, k, codes_tiled, sf_tiled,
+                                          (hipStream_t)stream));
+}
+
+int32_t nvfp4_mx_gemm(const uint8_t* a_tiled, const uint8_t* a_sf_tiled, const float* a_g,
+                      int64_t a_group_rows, const uint8_t* w_tiled, const uint8_t* w_sf_tiled,
+                      const float* w_gscale, void* y, int64_t B, int64_t N, int64_t K, void* stream) {
+  if (B < 0 || N <= 0 || K <= 0 || (N % 32) != 0 || (K % 128) != 0 || a_group_rows < 1)
+    return NVFP4_EINVAL;
+  if (B > 0 && (B % a_group_rows) != 0) return NVFP4_EINVAL;
+  if (B == 0) return NVFP4_OK;
+  if (!a_tiled || !a_sf_tiled || !a_g || !w_tiled || !w_sf_tiled || !w_gscale || !y) return NVFP4_EINVAL;
+  if (((uintptr_t)a_tiled % 16) != 0 || ((uintptr_t)w_tiled % 16) != 0 || !aligned4(a_sf_tiled) ||
+      !aligned4(w_sf_tiled) || !aligned4(a_g) || !aligned4(w_gscale) || ((uintptr_t)y % 8) != 0)
+    return NVFP4_EINVAL;
+  if (B > 0x7FFFFFE0LL || N > 0x7FFFFFE0LL || K > (1LL << 24)) return NVFP4_EUNSUPPORTED;
+  if (((B + 255) / 256) * ((N + 255) / 256) > 0x7FFFFFFFLL) return NVFP4_EUNSUPPORTED;
+  const int32_t ds = device_status();
+  if (ds != NVFP4_OK) return ds;
+  nvfp4::MxGemmArgs g{a_tiled, a_sf_tiled, a_g, a_group_rows, w_tiled, w_sf_tiled, w_gscale, y, B, N, K};
+  return hip_status(nvfp4::launch_mx_gemm(g, (hipStream_t)stream));
+}
+
 int32_t nvfp4_act_quant(const void* x, int32_t dtype, int64_t rows, int64_t k_out, int32_t act,
                         uint8_t* codes, uint8_t* sf, float* g_dec, float* scale_out, void* stream) {
   return quantize_common(x, dtype, rows, k_out, act, 1, codes, sf, g_dec, scale_out, nullptr, 0,

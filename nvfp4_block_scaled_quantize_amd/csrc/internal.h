@@ -26,6 +26,8 @@ struct QuantArgs {
   float* parts;        // workspace: [groups, nparts] partial maxima (group_rows > 1)
   int nparts;
   int num_cus;         // compute units of the current device (persistent grids)
+  int mx;              // MXFP4 variant: 32-element blocks with E8M0 scale bytes
+  int tiled;           // MXFP4 only: codes / scale bytes in the MX tile layout
 };
 
 // Number of partial maxima per group the per-group path uses.
@@ -69,6 +71,23 @@ struct MoeArgs {
   size_t workspace_bytes;
   int num_cus;         // compute units of the current device (work split)
 };
+
+// MXFP4 variant: the MX tile permutation and the block-scaled MFMA GEMM.
+struct MxGemmArgs {
+  const uint8_t* a;    // activation code tiles
+  const uint8_t* as;   // activation scale tiles
+  const float* ag;     // activation globals, one per a_group_rows rows
+  int64_t a_group_rows;
+  const uint8_t* w;    // weight code tiles
+  const uint8_t* ws;   // weight scale tiles
+  const float* wg;     // one weight global
+  void* y;             // [B, N] fp16
+  int64_t B, N, K;
+};
+
+hipError_t launch_mx_tile(const uint8_t* codes, const uint8_t* sf, int64_t rows, int64_t K,
+                          uint8_t* codes_tiled, uint8_t* sf_tiled, hipStream_t s);
+hipError_t launch_mx_gemm(const MxGemmArgs& g, hipStream_t s);
 
 size_t moe_workspace_bytes(int tokens, int experts, int top_k, int hidden, int inter);
 hipError_t launch_moe(const MoeArgs& m, hipStream_t s);

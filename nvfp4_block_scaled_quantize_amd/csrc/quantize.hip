@@ -30,6 +30,13 @@
 // reduces them to one maximum per group, and the row kernel uses that instead
 // of its own row's.
 //
+// MXFP4 variant (the UE8M0_SF switch of the block helper in the same pull
+// request): the same row kernel with 32-element blocks -- four adjacent lanes'
+// units -- and an E8M0 scale byte per block, the smallest power of two at or
+// above (amax_b / 6) * g_enc.  It can write the MX tile layout the
+// block-scaled MFMA GEMM reads (32-row groups, one 16-byte lane piece per 32
+// codes); then the padding rows of the last group are written as zeros.
+//
 // A scalar fallback handles inputs that are not 16-byte aligned (or codes not
 // 4-byte aligned) and rows longer than the register cache, with identical
 // results (same article, "Production Pitfalls & Hard Lessons", item 1).
@@ -470,6 +477,122 @@ void launch_rows(const QuantArgs& a, hipStream_t s) {
   }
 }
 
+// ---------------------------------------------------------------- MXFP4 variant
+
+// E8M0 byte of a 32-block and its encode factor: the smallest power of two x
+// >= (amax_b / 6) * g_enc, at most 2^127 (byte 254, also for NaN), at least
+// 2^-127 (byte 0); c = x * g_dec, enc = 1 / c (0 if c == 0).
+__device__ __forceinline__ uint32_t mx_block_scale(float amax_b, float g_enc, float g_dec,
+                                                   float& enc) {
+  const float sf_f = __builtin_fminf(div6_f32(amax_b) * g_enc, 0x1p127f);
+  const uint32_t b = __float_as_uint(sf_f);   // sf_f >= +0: amax_b >= 0, g_enc >= 0
+  uint32_t e;
+  if (b <= 0x00400000u) e = 0;                // at most 2^-127 (and +0)
+  else if (b < 0x00800000u) e = 1;            // subnormal above 2^-127: 2^-126
+  else e = (b >> 23) + ((b & 0x7FFFFFu) != 0u ? 1u : 0u);
+  const float x = (e == 0) ? 0x1p-127f : __uint_as_float(e << 23);
+  const float c = x * g_dec;
+  enc = (c == 0.0f) ? 0.0f : 1.0f / c;
+  return e;
+}
+
+// Byte offsets of unit q (8 codes, k = 8q) and of block b of row r in the MX
+// tile layout (nch64 = K/64 code tiles and nch128 = K/128 scale tiles per
+// 32-row group).
+__device__ __forceinline__ int64_t mx_code_pos(int64_t r, int q, int nch64) {
+  const int64_t tile = (r >> 5) * nch64 + (q >> 3);
+  return (tile * 64 + (r & 31) + 32 * ((q >> 2) & 1)) * 16 + 4 * (q & 3);
+}
+__device__ __forceinline__ int64_t mx_scale_pos(int64_t r, int b, int nch128) {
+  const int64_t tile = (r >> 5) * nch128 + (b >> 2);
+  return (tile * 64 + (r & 31) + 32 * (b & 1)) * 2 + ((b >> 1) & 1);
+}
+
+// MXFP4 row kernel: as quant_rows_vec, with the block amax over a lane quad.
+template <int DT, int ACT, int L, bool TILED>
+__global__ void __launch_bounds__(kMaxThreads)
+mx_quant_rows(const uint16_t* __restrict__ x, int64_t rows, int64_t k_out, int units,
+              uint8_t* __restrict__ codes, uint8_t* __restrict__ sf, float* __restrict__ g_dec,
+              const float* __restrict__ parts, int64_t group_rows, int nparts) {
+  __shared__ float red[kMaxThreads / 64];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x, T = blockDim.x;
+  const int nch64 = (int)(k_out / 64), nch128 = (int)(k_out / 128);
+  if (TILED && row >= rows) {   // padding row of the last 32-row group
+    for (int q = tid; q < units; q += T)
+      *reinterpret_cast<uint32_t*>(codes + mx_code_pos(row, q, nch64)) = 0u;
+    for (int b = tid; b < units / 4; b += T) sf[mx_scale_pos(row, b, nch128)] = 0;
+    return;
+  }
+  const int64_t k_in = (ACT == kActSwiglu) ? 2 * k_out : k_out;
+  const uint16_t* xr = x + row * k_in;
+  u32x4 rg[L], ru[L];
+  load_units<ACT, L>(xr, k_out, units, tid, T, rg, ru);
+  float y[L][8];
+  float am[L];
+  float tmax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    unit_values<DT, ACT>(rg[i], ru[i], y[i]);
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(y[i][e]));
+    m = __builtin_fmaxf(m, dpp_f32<0xB1>(m));   // lane ^ 1
+    m = __builtin_fmaxf(m, dpp_f32<0x4E>(m));   // lane ^ 2: the quad holds one 32-block
+    am[i] = (tid + i * T < units) ? m : 0.0f;
+    tmax = __builtin_fmaxf(tmax, am[i]);
+  }
+  if (parts != nullptr) tmax = partials_max(parts, row, group_rows, nparts);
+  const float amax = block_max(tmax, red);
+  float g_enc, gd;
+  global_scales(amax, g_enc, gd);
+  if (tid == 0) {
+    if (group_rows == 1) g_dec[row] = gd;
+    else if (row % group_rows == 0) g_dec[row / group_rows] = gd;
+  }
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const int q = tid + i * T;
+    if (q >= units) continue;
+    float enc;
+    const uint32_t sbyte = mx_block_scale(am[i], g_enc, gd, enc);
+    const uint32_t w = pack8_e2m1(y[i], enc);
+    if constexpr (TILED) {
+      __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(codes + mx_code_pos(row, q, nch64)));
+      if ((tid & 3) == 0) sf[mx_scale_pos(row, q >> 2, nch128)] = (uint8_t)sbyte;
+    } else {
+      __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(codes + row * (k_out / 2) + 4 * (int64_t)q));
+      if ((tid & 3) == 0) sf[row * (k_out / 32) + (q >> 2)] = (uint8_t)sbyte;
+    }
+  }
+}
+
+template <int DT, int ACT, bool TILED>
+void launch_mx_rows(const QuantArgs& a, hipStream_t s) {
+  const int units = (int)(a.k_out / 8);
+  int L = (units + kMaxThreads - 1) / kMaxThreads;
+  L = L <= 1 ? 1 : L <= 2 ? 2 : L <= 4 ? 4 : L <= 8 ? 8 : kMaxUnits;
+  const int threads = round64((units + L - 1) / L);
+  const int64_t grid = TILED ? (a.rows + 31) / 32 * 32 : a.rows;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(threads), 0, s, (const uint16_t*)a.x, a.rows,
+                       a.k_out, units, a.codes, a.sf, a.g_dec, a.parts, a.group_rows, a.nparts);
+  };
+  switch (L) {
+    case 1: go(mx_quant_rows<DT, ACT, 1, TILED>); break;
+    case 2: go(mx_quant_rows<DT, ACT, 2, TILED>); break;
+    case 4: go(mx_quant_rows<DT, ACT, 4, TILED>); break;
+    case 8: go(mx_quant_rows<DT, ACT, 8, TILED>); break;
+    default: go(mx_quant_rows<DT, ACT, kMaxUnits, TILED>); break;
+  }
+}
+
+template <int DT, int ACT>
+void launch_mx(const QuantArgs& a, hipStream_t s) {
+  if (a.tiled) launch_mx_rows<DT, ACT, true>(a, s);
+  else launch_mx_rows<DT, ACT, false>(a, s);
+}
+
 }  // namespace
 
 int quant_num_parts(int64_t group_elems) {
@@ -500,6 +623,22 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
     b.nparts = 1;
   } else {
     b.parts = nullptr;
+  }
+  if (a.mx) {
+    if (a.dtype == kBf16) {
+      switch (a.act) {
+        case kActSwiglu: launch_mx<0, kActSwiglu>(b, s); break;
+        case kActRelu2: launch_mx<0, kActRelu2>(b, s); break;
+        default: launch_mx<0, kActNone>(b, s); break;
+      }
+    } else {
+      switch (a.act) {
+        case kActSwiglu: launch_mx<1, kActSwiglu>(b, s); break;
+        case kActRelu2: launch_mx<1, kActRelu2>(b, s); break;
+        default: launch_mx<1, kActNone>(b, s); break;
+      }
+    }
+    return hipGetLastError();
   }
   if (a.dtype == kBf16) {
     switch (a.act) {

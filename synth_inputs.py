@@ -120,3 +120,26 @@ def random_nvfp4_operands(B: int, N: int, K: int, seed: int = SEED, config: int 
         "w_sf": g.integers(0, 0x7F, size=(N, K // 16), dtype=np.uint8),
         "w_g": np.array([1.0 / 2688.0], np.float32),
     }
+
+
+def random_mx_operands(B: int, N: int, K: int, seed: int = SEED, config: int = 61) -> dict:
+    """Arbitrary valid MXFP4 GEMM operands drawn directly in the stored formats
+    (no quantization involved): uniform code bytes, E8M0 scale bytes uniform in
+    [127-12, 127+3] (finite powers of two), per-row activation globals in
+    [2^-4, 1) and one weight global in [2^-3, 2^-1), from uniform exponents and
+    mantissa bits (outputs stay in the normal fp16 range).  For size tests where
+    quantizing a real input on the CPU would be too slow."""
+    g = rng(config, 0, seed)
+
+    def pos_floats(n, lo, hi):
+        ex = g.integers(127 + lo, 127 + hi, size=n, dtype=np.uint32)
+        return (np.left_shift(ex, 23) | g.integers(0, 1 << 23, size=n, dtype=np.uint32)).view(np.float32)
+
+    return {
+        "a_codes": g.integers(0, 256, size=(B, K // 2), dtype=np.uint8),
+        "a_sf": g.integers(127 - 12, 127 + 4, size=(B, K // 32), dtype=np.uint8),
+        "a_g": pos_floats(B, -4, 0),
+        "w_codes": g.integers(0, 256, size=(N, K // 2), dtype=np.uint8),
+        "w_sf": g.integers(127 - 12, 127 + 4, size=(N, K // 32), dtype=np.uint8),
+        "w_g": pos_floats(1, -3, -1),
+    }

@@ -119,3 +119,29 @@ def test_pretiled_validation_without_gpu(nv):
     assert L.nvfp4_gemm_pretiled(p, p, p, p, p, p, 4, 48, 192, None, 0, None) == nv.NVFP4_EINVAL
     assert L.nvfp4_gemm_pretiled(p, p, ctypes.c_void_p(4104), p, p, p, 4, 48, 256, None, 0, None) == nv.NVFP4_EINVAL
     assert L.nvfp4_gemm_pretiled(p, p4, p, p, p, p, 0, 48, 256, None, 0, None) == nv.NVFP4_OK   # B == 0
+
+
+def test_mx_validation_without_gpu(nv):
+    L = nv.lib()
+    p = ctypes.c_void_p(4096)
+    # quantizer: k % 32 (rows) / % 128 (tiled), activation only per token,
+    # unaligned input, bad layout, k beyond the register cache
+    assert L.nvfp4_mx_quantize(p, 0, 4, 48, 0, 1, nv.MX_ROWS, p, p, p, None, 0, None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_mx_quantize(p, 0, 4, 96, 0, 1, nv.MX_TILED, p, p, p, None, 0, None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_mx_quantize(p, 0, 4, 128, 1, 2, nv.MX_ROWS, p, p, p, None, 0, None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_mx_quantize(ctypes.c_void_p(4104), 0, 4, 128, 0, 1, nv.MX_ROWS, p, p, p, None, 0,
+                               None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_mx_quantize(p, 0, 4, 128, 0, 1, 2, p, p, p, None, 0, None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_mx_quantize(p, 0, 4, 65536, 0, 1, nv.MX_ROWS, p, p, p, None, 0, None) == nv.NVFP4_EUNSUPPORTED
+    assert L.nvfp4_mx_quantize(p, 0, 4, 128, 0, 4, nv.MX_ROWS, p, p, p, None, 0, None) == nv.NVFP4_EWORKSPACE
+    assert L.nvfp4_mx_quantize(p, 0, 0, 128, 0, 1, nv.MX_ROWS, p, p, p, None, 0, None) == nv.NVFP4_OK
+    # tile permutation: k % 128, alignment
+    assert L.nvfp4_mx_tile(p, p, 40, 192, p, p, None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_mx_tile(ctypes.c_void_p(4100), p, 40, 256, p, p, None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_mx_tile(p, p, 0, 256, p, p, None) == nv.NVFP4_OK
+    # GEMM: N % 32, K % 128, B % a_group_rows, alignment, B == 0
+    assert L.nvfp4_mx_gemm(p, p, p, 1, p, p, p, p, 4, 48, 256, None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_mx_gemm(p, p, p, 1, p, p, p, p, 4, 64, 192, None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_mx_gemm(p, p, p, 3, p, p, p, p, 4, 64, 256, None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_mx_gemm(p, p, p, 1, p, p, p, ctypes.c_void_p(4100), 4, 64, 256, None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_mx_gemm(p, p, p, 1, p, p, p, p, 0, 64, 256, None) == nv.NVFP4_OK
