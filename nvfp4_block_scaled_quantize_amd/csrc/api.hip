@@ -139,7 +139,7 @@ int32_t nvfp4_mx_quantize(const void* x, int32_t dtype, int64_t rows, int64_t k_
   if (rows == 0) return NVFP4_OK;
   if (!x || !codes || !sf || !g_dec) return NVFP4_EINVAL;
   if (((uintptr_t)x % 16) != 0 || !aligned4(codes) || !aligned4(g_dec)) return NVFP4_EINVAL;
-  if (k_out > 32768 || rows > 0x7FFFFFE0LL) return NVFP4_EUNSUPPORTED;
+  if (k_out > 32768 || rows > 0x7FFFFF00LL) return NVFP4_EUNSUPPORTED;   // grid of whole 256-row sets
   nvfp4::QuantArgs a{};
   a.x = x; a.dtype = dtype; a.act = act; a.rows = rows; a.k_out = k_out; a.group_rows = group_rows;
   a.codes = codes; a.sf = sf; a.g_dec = g_dec; a.scale_out = nullptr; a.parts = nullptr;

@@ -151,16 +151,25 @@ mx_gemm_wide(const uint8_t* __restrict__ a, const uint8_t* __restrict__ as,
   const uint8_t* wsbase = ws + (size_t)gn0 * K;
   const uint8_t* asbase = as + (size_t)gm0 * K;
 
-  auto issue = [&](unsigned char* buf, int st) {
+  // copy instructions [lo, hi) of stage st (0-3 weight codes, 4-7 activation
+  // codes, 8 weight scales, 9 activation scales) into buffer buf
+  auto issue_part = [&](unsigned char* buf, int st, int lo, int hi) __attribute__((always_inline)) {
     const uint32_t l0 = mx_lds_addr(buf);
-    const uint8_t* wst = wbase + (size_t)st * 2048;
-    const uint8_t* ast = abase + (size_t)st * 2048;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) mx_dma16(wst, wofs[j], l0 + kMwWOff + (4 * wave + j) * 1024);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) mx_dma16(ast, aofs[j], l0 + kMwAOff + (4 * wave + j) * 1024);
-    mx_dma4(wsbase + (size_t)st * 128, wsofs, l0 + kMwWSOff + wave * 256);
-    mx_dma4(asbase + (size_t)st * 128, asofs, l0 + kMwASOff + wave * 256);
+    for (int idx = 0; idx < kMwLoads; ++idx) {
+      if (idx < lo || idx >= hi) continue;
+      if (idx < 4)
+        mx_dma16(wbase + (size_t)st * 2048, wofs[idx], l0 + kMwWOff + (4 * wave + idx) * 1024);
+      else if (idx < 8)
+        mx_dma16(abase + (size_t)st * 2048, aofs[idx - 4], l0 + kMwAOff + (4 * wave + idx - 4) * 1024);
+      else if (idx == 8)
+        mx_dma4(wsbase + (size_t)st * 128, wsofs, l0 + kMwWSOff + wave * 256);
+      else
+        mx_dma4(asbase + (size_t)st * 128, asofs, l0 + kMwASOff + wave * 256);
+    }
+  };
+  auto issue = [&](unsigned char* buf, int st) __attribute__((always_inline)) {
+    issue_part(buf, st, 0, kMwLoads);
   };
 
   v16f acc[4][4];
@@ -171,49 +180,123 @@ mx_gemm_wide(const uint8_t* __restrict__ a, const uint8_t* __restrict__ as,
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  auto kstep = [&](const unsigned char* st, const uint32_t (&sw)[4], const uint32_t (&sa)[4],
-                   auto kkc) __attribute__((always_inline)) {
-    constexpr int KK = decltype(kkc)::value;
-    v8i wf[4], af[4];
+  // Operand fragments of one 64-k step (four weight and four activation
+  // 32-row blocks) and the scale registers of a stage.
+  struct Frags {
+    v8i w[4], a[4];
+  };
+  struct Scales {
+    uint32_t w[4], a[4];
+  };
+  auto read_frags = [&](const unsigned char* st, int kk, Frags& f) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      wf[i] = fp4_operand(*reinterpret_cast<const u32x4*>(st + kMwWOff + ((4 * wn + i) * 2 + KK) * 1024 + 16 * lane));
+      f.w[i] = fp4_operand(*reinterpret_cast<const u32x4*>(st + kMwWOff + ((4 * wn + i) * 2 + kk) * 1024 + 16 * lane));
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      af[j] = fp4_operand(*reinterpret_cast<const u32x4*>(st + kMwAOff + ((4 * wm + j) * 2 + KK) * 1024 + 16 * lane));
+      f.a[j] = fp4_operand(*reinterpret_cast<const u32x4*>(st + kMwAOff + ((4 * wm + j) * 2 + kk) * 1024 + 16 * lane));
+  };
+  auto read_scales = [&](const unsigned char* st, Scales& c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c.w[i] = *reinterpret_cast<const uint16_t*>(st + kMwWSOff + (4 * wn + i) * 128 + 2 * lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c.a[j] = *reinterpret_cast<const uint16_t*>(st + kMwASOff + (4 * wm + j) * 128 + 2 * lane);
+  };
+  // Empty volatile asm taking accumulators as inputs: the MFMAs producing
+  // them stay above it (volatile asm keeps its order against the copies and
+  // the barrier, which plain MFMA builtins do not).
+  auto pin_row = [&](int i) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" ::"a"(acc[i][j]));
+  };
+  auto mfmas = [&](const Frags& f, const Scales& c, auto kkc) __attribute__((always_inline)) {
+    constexpr int KK = decltype(kkc)::value;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_mx<KK>(wf[i], af[j], acc[i][j], sw[i], sa[j]);
-  };
-  auto compute = [&](const unsigned char* st) __attribute__((always_inline)) {
-    uint32_t sw[4], sa[4];
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_mx<KK>(f.w[i], f.a[j], acc[i][j], c.w[i], c.a[j]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sw[i] = *reinterpret_cast<const uint16_t*>(st + kMwWSOff + (4 * wn + i) * 128 + 2 * lane);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sa[j] = *reinterpret_cast<const uint16_t*>(st + kMwASOff + (4 * wm + j) * 128 + 2 * lane);
-    kstep(st, sw, sa, std::integral_constant<int, 0>());
-    kstep(st, sw, sa, std::integral_constant<int, 1>());
+    for (int i = 0; i < 4; ++i) pin_row(i);
   };
-  // one stage: wait for its copies (stages s+1, s+2 may stay in flight),
-  // barrier, start stage s+3's copies into the buffer freed by stage s-1
-  auto step = [&](const unsigned char* cur, unsigned char* next3, int s) __attribute__((always_inline)) {
-    if (s + 2 < nstages) mx_wait_vmcnt<2 * kMwLoads>();
-    else if (s + 1 < nstages) mx_wait_vmcnt<kMwLoads>();
-    else mx_wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    if (s + 3 < nstages) issue(next3, s + 3);
-    compute(cur);
+  // The same MFMAs in four groups of four with stage st's copies issued
+  // between the groups, so the copy instructions' issue time overlaps the
+  // matrix pipe instead of idling it.
+  auto mfmas_copy = [&](const Frags& f, const Scales& c, auto kkc, unsigned char* buf, int st)
+                        __attribute__((always_inline)) {
+    constexpr int KK = decltype(kkc)::value;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // the group's weight scale passes through an empty volatile asm placed
+      // after the previous copies, so the compiler cannot hoist the group's
+      // MFMAs above them
+      uint32_t sw = c.w[i];
+      if (i > 0) asm volatile("" : "+v"(sw));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_mx<KK>(f.w[i], f.a[j], acc[i][j], sw, c.a[j]);
+      pin_row(i);
+      __builtin_amdgcn_sched_barrier(0);
+      if (st < nstages) issue_part(buf, st, (i * kMwLoads) / 4, ((i + 1) * kMwLoads) / 4);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Stage s (buffer cur): the fragments of its first 64-k step are already
+  // in registers (f0, c0).  Read the second step's fragments, run the first
+  // step's 16 MFMAs; then wait for stage s+1's copies, barrier (every wave
+  // is past its reads of stage s-1), start stage s+3's copies into stage
+  // s-1's buffer, read stage s+1's first-step fragments into (f0n, c0n), and
+  // run the second step's MFMAs while those reads land.
+  auto stage = [&](const unsigned char* cur, const unsigned char* next1, unsigned char* next3, int s,
+                   Frags& f0, Scales& c0, Frags& f0n, Scales& c0n) __attribute__((always_inline)) {
+    // (the scheduling barriers keep the compiler from hoisting the barrier
+    // and the next stage's reads above the first step's MFMAs)
+    // the second step's reads go out after the first four MFMAs, so the wait
+    // for the first step's operands (read during the previous stage) does not
+    // also wait for them
+    Frags f1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[0][j] = mfma_mx<0>(f0.w[0], f0.a[j], acc[0][j], c0.w[0], c0.a[j]);
+    pin_row(0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(cur, 1, f1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 1; i < 4; ++i) {
+      uint32_t sw = c0.w[i];
+      asm volatile("" : "+v"(sw));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_mx<0>(f0.w[i], f0.a[j], acc[i][j], sw, c0.a[j]);
+      pin_row(i);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (s + 1 < nstages) {
+      if (s + 2 < nstages) mx_wait_vmcnt<kMwLoads>();
+      else mx_wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      read_scales(next1, c0n);
+      read_frags(next1, 0, f0n);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas_copy(f1, c0, std::integral_constant<int, 1>(), next3, s + 3);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   issue(lds0, 0);
   if (nstages > 1) issue(lds1, 1);
   if (nstages > 2) issue(lds2, 2);
+  if (nstages > 2) mx_wait_vmcnt<2 * kMwLoads>();
+  else if (nstages > 1) mx_wait_vmcnt<kMwLoads>();
+  else mx_wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  Frags fa, fb;
+  Scales ca, cb;
+  read_frags(lds0, 0, fa);
+  read_scales(lds0, ca);
   for (int s = 0; s < nstages; s += 4) {
-    step(lds0, lds3, s);
-    if (s + 1 < nstages) step(lds1, lds0, s + 1);
-    if (s + 2 < nstages) step(lds2, lds1, s + 2);
-    if (s + 3 < nstages) step(lds3, lds2, s + 3);
+    stage(lds0, lds1, lds3, s, fa, ca, fb, cb);
+    if (s + 1 < nstages) stage(lds1, lds2, lds0, s + 1, fb, cb, fa, ca);
+    if (s + 2 < nstages) stage(lds2, lds3, lds1, s + 2, fa, ca, fb, cb);
+    if (s + 3 < nstages) stage(lds3, lds0, lds2, s + 3, fb, cb, fa, ca);
   }
 
   // lane: row m (activation) = lane & 31 of block j; columns n = 8q + 4h + 0..3

@@ -515,7 +515,15 @@ mx_quant_rows(const uint16_t* __restrict__ x, int64_t rows, int64_t k_out, int u
               uint8_t* __restrict__ codes, uint8_t* __restrict__ sf, float* __restrict__ g_dec,
               const float* __restrict__ parts, int64_t group_rows, int nparts) {
   __shared__ float red[kMaxThreads / 64];
-  const int64_t row = blockIdx.x;
+  int64_t row = blockIdx.x;
+  if constexpr (TILED) {
+    // the 32 rows of a row group run on one XCD (consecutive workgroup ids go
+    // to different XCDs), so each tile's 16-byte pieces meet in one L2 and
+    // leave it as whole lines; ids past the last group exit
+    const int64_t xcd = row & 7, slot = row >> 3;
+    row = ((slot >> 5) * 8 + xcd) * 32 + (slot & 31);
+    if (row >= (rows + 31) / 32 * 32) return;
+  }
   const int tid = threadIdx.x, T = blockDim.x;
   const int nch64 = (int)(k_out / 64), nch128 = (int)(k_out / 128);
   if (TILED && row >= rows) {   // padding row of the last 32-row group
@@ -558,7 +566,10 @@ mx_quant_rows(const uint16_t* __restrict__ x, int64_t rows, int64_t k_out, int u
     const uint32_t sbyte = mx_block_scale(am[i], g_enc, gd, enc);
     const uint32_t w = pack8_e2m1(y[i], enc);
     if constexpr (TILED) {
-      __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(codes + mx_code_pos(row, q, nch64)));
+      // a plain store: the 16-byte pieces of a tile's lines come from 32
+      // workgroups and must merge in L2 (a streaming store would send each
+      // piece to memory as a partial line)
+      *reinterpret_cast<uint32_t*>(codes + mx_code_pos(row, q, nch64)) = w;
       if ((tid & 3) == 0) sf[mx_scale_pos(row, q >> 2, nch128)] = (uint8_t)sbyte;
     } else {
       __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(codes + row * (k_out / 2) + 4 * (int64_t)q));
@@ -573,7 +584,7 @@ void launch_mx_rows(const QuantArgs& a, hipStream_t s) {
   int L = (units + kMaxThreads - 1) / kMaxThreads;
   L = L <= 1 ? 1 : L <= 2 ? 2 : L <= 4 ? 4 : L <= 8 ? 8 : kMaxUnits;
   const int threads = round64((units + L - 1) / L);
-  const int64_t grid = TILED ? (a.rows + 31) / 32 * 32 : a.rows;
+  const int64_t grid = TILED ? (a.rows + 255) / 256 * 256 : a.rows;   // whole sets of 8 row groups
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(threads), 0, s, (const uint16_t*)a.x, a.rows,
                        a.k_out, units, a.codes, a.sf, a.g_dec, a.parts, a.group_rows, a.nparts);
