@@ -9,8 +9,8 @@ prefill GEMM B=4096, K=8192, N=8192 (bf16 activations ~N(0,1), weights
 ~N(0,0.02), FP16 output); `value` is whole-step TFLOP/s (2*B*N*K per step).
 The same GEMM on the plain [N, K/2] weight layout (nvfp4_gemm) is timed after
 the steps and reported under "workloads".  The other workloads (decode GEMM, fused SwiGLU quantize,
-quantize + GEMM small case, MoE) are measured after it and reported under
-"workloads".
+quantize + GEMM small case, the MXFP4 variant's prefill step and decode GEMM
+on the FP4 MFMA, MoE) are measured after it and reported under "workloads".
 
 Timing: inputs are resident in HBM before the timed region; W warmup steps,
 then exactly K steps between synchronizations, timed with HIP events on the
@@ -49,7 +49,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--quick", action="store_true", help="skip the secondary workloads and the CPU baseline")
     p.add_argument("--no-cpu", action="store_true")
-    p.add_argument("--only", choices=["prefill", "decode", "swiglu", "quant", "small", "moe", "copy"],
+    p.add_argument("--only", choices=["prefill", "decode", "swiglu", "quant", "small", "moe", "copy",
+                                      "mx_prefill", "mx_decode"],
                    help="run one workload and print its measurement (for profiler runs)")
     return p.parse_args()
 
@@ -256,6 +257,76 @@ def run_moe(torch, nv, si, iters=None):
                 hbm_frac=by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, flops=2.0 * T * c["top_k"] * (2 * Hd * I))
 
 
+def mx_gemm_bytes(B, N, K):
+    """Algorithmic bytes of one MX GEMM call: codes, E8M0 bytes and globals of
+    both operands read once (padding rows excluded), output written once."""
+    return B * K // 2 + B * K // 32 + B * 4 + N * K // 2 + N * K // 32 + 4 + B * N * 2
+
+
+def mx_quant_bytes(rows, k):
+    return rows * k * 2 + rows * k // 2 + rows * k // 32 + rows * 4
+
+
+def run_mx_prefill(torch, nv, si, steps, warmup):
+    """MXFP4 variant of the prefill step: per-token MX quantization of the same
+    [4096, 8192] bf16 activations straight into the MX tile layout, then the
+    block-scaled FP4 MFMA GEMM against the same weights, MX-quantized per tensor
+    into the tile layout before timing."""
+    c = si.CONFIGS["C3"]
+    B, K, N = c["B"], c["K"], c["N"]
+    dev = torch.device("cuda:0")
+    a, w = si.gemm_inputs("C3")
+    x = a.to(dev)
+    wt = nv.mx_quantize(w.to(dev), group_rows=N, tiled=True)
+    del w
+    stream = torch.cuda.current_stream()
+    qa = nv.mx_quantize(x, tiled=True)
+    y = torch.empty((B, N), dtype=torch.float16, device=dev)
+
+    def step(tq=None, tg=None):
+        fq = lambda: nv.mx_quantize(x, tiled=True, out=qa)
+        fg = lambda: nv.mx_gemm(qa, qa["g_dec"], wt, wt["g_dec"], out=y)
+        tq(fq) if tq else fq()
+        tg(fg) if tg else fg()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    tq, tg = EventTimer(torch, stream), EventTimer(torch, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step(tq, tg)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+    flops = 2.0 * B * N * K
+    ms_g, ms_q = tg.mean_ms(), tq.mean_ms()
+    return dict(B=B, K=K, N=N, ms_step=ms_step, ms_gemm=ms_g, ms_quant=ms_q,
+                gemm_TFLOPs=flops / (ms_g * 1e-3) / 1e12,
+                gemm_frac_fp4_peak=flops / (ms_g * 1e-3) / 1e12 / FP4_MFMA_PEAK_TFLOPS,
+                quant_GBps=mx_quant_bytes(B, K) / (ms_q * 1e-3) / 1e9,
+                quant_hbm_frac=mx_quant_bytes(B, K) / (ms_q * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                step_TFLOPs=flops / (ms_step * 1e-3) / 1e12)
+
+
+def run_mx_decode(torch, nv, si, B):
+    """MX decode GEMM (K=4096, N=8192) with the weight tiles rotated through 32
+    copies (> 512 MB) past the Infinity Cache; HIP-graph replay."""
+    c = si.CONFIGS["C2"]
+    K, N = c["K"], c["N"]
+    dev = torch.device("cuda:0")
+    a, w = si.gemm_inputs("C2", B=B)
+    w0 = nv.mx_quantize(w.to(dev), group_rows=N, tiled=True)
+    Ws = [dict(w0, codes=w0["codes"].clone(), sf=w0["sf"].clone()) for _ in range(32)]
+    qa = nv.mx_quantize(a.to(dev), tiled=True)
+    y = torch.empty((B, N), dtype=torch.float16, device=dev)
+    ms = graph_time_ms(torch, [(lambda Wi=Wi: nv.mx_gemm(qa, qa["g_dec"], Wi, Wi["g_dec"], out=y)) for Wi in Ws])
+    by = mx_gemm_bytes(B, N, K)
+    return dict(B=B, us_gemm=ms * 1e3, gemm_bytes=by, GBps=by / (ms * 1e-3) / 1e9,
+                hbm_frac=by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+
+
 def run_copy(torch):
     """A plain 256 MiB device copy, three times: the reference for scaling the
     FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -329,7 +400,9 @@ def main():
               "quant": lambda: run_quant_rotating(torch, nv, si),
               "small": lambda: run_small(torch, nv, si),
               "moe": lambda: run_moe(torch, nv, si),
-              "copy": lambda: run_copy(torch)}[args.only]
+              "copy": lambda: run_copy(torch),
+              "mx_prefill": lambda: run_mx_prefill(torch, nv, si, 3, 1),
+              "mx_decode": lambda: {B: run_mx_decode(torch, nv, si, B) for B in (1, 4, 8)}}[args.only]
         print(json.dumps({"only": args.only, "result": fn()}, default=str), flush=True)
         return
     log("prefill: act_quant [4096,8192] + gemm 4096x8192x8192, %d warmup + %d steps" % (args.warmup, args.steps))
@@ -361,6 +434,13 @@ def main():
         log("small quantize + gemm")
         workloads["small_C1"] = {k: (round(v, 4) if isinstance(v, float) else v)
                                  for k, v in run_small(torch, nv, si).items()}
+        log("mxfp4 prefill step (E8M0 scales, FP4 MFMA)")
+        workloads["mx_prefill_C3"] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                      for k, v in run_mx_prefill(torch, nv, si, args.steps, args.warmup).items()}
+        for B in (1, 4, 8):
+            log("mxfp4 decode B=%d" % B)
+            workloads["mx_decode_C2_B%d" % B] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                                 for k, v in run_mx_decode(torch, nv, si, B).items()}
         try:
             log("moe")
             workloads["moe_C5"] = {k: (round(v, 4) if isinstance(v, float) else v)
