@@ -290,7 +290,7 @@ int32_t nvfp4_mx_tile(const uint8_t* codes, const uint8_t* sf, int64_t rows, int
  *   a_g                 : [B / a_group_rows] float activation globals (1 = per token)
  *   w_tiled, w_sf_tiled : weight tiles (N rows), e.g. from nvfp4_mx_tile
  *   w_gscale            : one device float
- *   y                   : [B, N] fp16, 8-byte aligned
+ *   y                   : [B, N] fp16, 16-byte aligned
  * Requires N % 32 == 0, K % 128 == 0, K <= 2^24, B % a_group_rows == 0;
  * tiles 16-byte and scale tiles, a_g, w_gscale 4-byte aligned.  B == 0 is a no-op.
  */

@@ -181,7 +181,7 @@ int32_t nvfp4_mx_gemm(const uint8_t* a_tiled, const uint8_t* a_sf_tiled, const f
   if (B == 0) return NVFP4_OK;
   if (!a_tiled || !a_sf_tiled || !a_g || !w_tiled || !w_sf_tiled || !w_gscale || !y) return NVFP4_EINVAL;
   if (((uintptr_t)a_tiled % 16) != 0 || ((uintptr_t)w_tiled % 16) != 0 || !aligned4(a_sf_tiled) ||
-      !aligned4(w_sf_tiled) || !aligned4(a_g) || !aligned4(w_gscale) || ((uintptr_t)y % 8) != 0)
+      !aligned4(w_sf_tiled) || !aligned4(a_g) || !aligned4(w_gscale) || ((uintptr_t)y % 16) != 0)
     return NVFP4_EINVAL;
   if (B > 0x7FFFFFE0LL || N > 0x7FFFFFE0LL || K > (1LL << 24)) return NVFP4_EUNSUPPORTED;
   if (((B + 255) / 256) * ((N + 255) / 256) > 0x7FFFFFFFLL) return NVFP4_EUNSUPPORTED;

@@ -23,7 +23,8 @@
 //    global -> LDS by global_load_lds_dwordx4/_dword, four LDS buffers (three
 //    stages in flight), one barrier per stage.  Every copy reads whole 1 KiB
 //    code tiles / 256 B of scale tiles, and every MFMA operand read is one
-//    contiguous 1 KiB ds_read_b128 (no bank conflicts).
+//    contiguous 1 KiB ds_read_b128 (no bank conflicts).  The fp16 output goes
+//    through LDS so that each store instruction writes whole row segments.
 //  * mx_gemm_skinny (B <= 32, decode): one workgroup per 32-row weight group,
 //    eight waves splitting K; each wave streams its code and scale tiles
 //    straight into registers, all of them issued before the first MFMA, and
@@ -299,25 +300,44 @@ mx_gemm_wide(const uint8_t* __restrict__ a, const uint8_t* __restrict__ as,
     if (s + 3 < nstages) stage(lds3, lds0, lds2, s + 3, fb, cb, fa, ca);
   }
 
-  // lane: row m (activation) = lane & 31 of block j; columns n = 8q + 4h + 0..3
-  // of block i for accumulator registers 4q .. 4q+3
+  // Epilogue through LDS: each wave writes its 128 x 128 block, scaled and
+  // rounded to fp16, row-major into its own stage buffer (row pitch 272 B:
+  // 128 rows x 272 B is exactly one buffer; the 16-byte skew per row spreads
+  // the 32 rows a store instruction touches over the banks), then stores it
+  // with 16-byte lanes, 4 rows x 256 contiguous bytes per instruction,
+  // instead of 16-byte pieces of 32 rows.  The barrier keeps the buffers'
+  // last stage intact until every wave has read it.
+  // Accumulator layout: lane holds row m = lane & 31 of block j and columns
+  // n = 8q + 4h + 0..3 of block i in registers 4q .. 4q+3.
+  __syncthreads();
+  unsigned char* eb = wave == 0 ? lds0 : wave == 1 ? lds1 : wave == 2 ? lds2 : lds3;
+  constexpr int kPitch = 272;
   const float gwv = *wg;
   const int h = lane >> 5;
+  const int mw = tm * kMwTile + 128 * wm;     // first activation row of this wave's block
+  const int nw = tn * kMwTile + 128 * wn;     // first weight row (output column)
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int m = tm * kMwTile + 128 * wm + 32 * j + (lane & 31);
-    if (m >= B) continue;
+    const int ml = 32 * j + (lane & 31);
+    const int m = min(mw + ml, B - 1);        // rows past B are written to LDS, never stored
     const float s = ag[m / a_group_rows] * gwv;
-    _Float16* yr = y + (int64_t)m * N;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int nb = tn * kMwTile + 128 * wn + 32 * i;
-      if (nb >= N) continue;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        store4(yr + nb + 8 * q + 4 * h, acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-               acc[i][j][4 * q + 3], s);
-    }
+      for (int q = 0; q < 4; ++q) {
+        v4h o = {(_Float16)(acc[i][j][4 * q] * s), (_Float16)(acc[i][j][4 * q + 1] * s),
+                 (_Float16)(acc[i][j][4 * q + 2] * s), (_Float16)(acc[i][j][4 * q + 3] * s)};
+        *reinterpret_cast<v4h*>(eb + ml * kPitch + 2 * (32 * i + 8 * q + 4 * h)) = o;
+      }
+  }
+  // only this wave reads what it wrote: a wave-local LDS wait suffices
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const int cr = lane >> 4, cc = lane & 15;   // 4 rows x 16 chunks of 16 bytes per instruction
+#pragma unroll 4
+  for (int r0 = 0; r0 < 128; r0 += 4) {
+    const int m = mw + r0 + cr, n = nw + 8 * cc;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(eb + (r0 + cr) * kPitch + 16 * cc);
+    if (m < B && n < N) *reinterpret_cast<u32x4*>(y + (int64_t)m * N + n) = v;
   }
 }
 
