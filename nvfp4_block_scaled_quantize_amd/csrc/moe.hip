@@ -12,18 +12,22 @@
 //                  order.
 //  2. lists      : one workgroup per expert writes the pairs (token, rank)
 //                  routed to it, in pair order, and their count.
-//  3. fc1        : grid (inter/256, experts), 8 waves x 32 weight rows.
-//                  Computes h = relu(x . W1^T * g1)^2 with
-//                  v_mfma_f32_16x16x32_f16: weights dequantized in registers
-//                  (exact in FP16) and streamed one 256-k chunk ahead, the
-//                  expert's tokens gathered from x into LDS in passes of 64.
-//                  h is stored in fp32 per pair, and the largest h of each
-//                  pair is folded into a per-pair maximum (integer max on the
-//                  fp32 bits: order independent).
-//  4. fc2        : grid (hidden/256, experts).  Same structure on h, which is
-//                  converted to FP16 after scaling by 2^-e (e = exponent of
-//                  the pair's maximum, so no pair can overflow FP16);
-//                  o = h . W2^T * g2 * 2^e, stored in fp32 per pair.
+//  3. fc1        : grid (inter/256 row tiles, experts, token passes), 8 waves
+//                  x 32 weight rows, v_mfma_f32_32x32x16_f16.  Weights are
+//                  dequantized in registers (exact in FP16) and loaded three
+//                  128-k chunks ahead; the expert's tokens are gathered from x
+//                  three chunks ahead and staged in LDS, in balanced passes of
+//                  at most 64 tokens (an expert with more tokens spreads over
+//                  several workgroups).  h = relu(x . W1^T * g1)^2 is stored
+//                  as FP16 scaled by 2^-et per (pair, 256-row tile), et the
+//                  exponent of the tile's largest h; the pair's overall
+//                  largest h is an integer max of fp32 bits (order
+//                  independent).
+//  4. fc2        : grid (hidden/256 row tiles, experts, token passes).  Same
+//                  structure on h, each tile rescaled by 2^(et - e) while
+//                  staged (e = exponent of the pair's largest h, so no pair
+//                  can overflow FP16); o = h . W2^T * g2 * 2^e in fp32 per
+//                  pair.
 //  5. combine    : out[t] = sum_j w[t,j] * o[t*top_k + j] in rank order, FP16.
 #include "device_common.h"
 #include "internal.h"
@@ -303,7 +307,7 @@ __device__ __forceinline__ v8h dequant8_w(uint32_t codes, _Float16 s16) {
 constexpr int kFwThreads = 512;
 constexpr int kFwRows = 256;              // weight rows per tile
 constexpr int kFwKC = 128;                // k per chunk
-constexpr int kFwTT = 5;                  // 32-token MFMA tiles per pass
+constexpr int kFwTT = 2;                  // 32-token MFMA tiles per pass
 constexpr int kFwTok = 32 * kFwTT;        // tokens per pass at most
 constexpr int kFwPitch = kFwKC + 8;       // halves per staged token row (+16 B skew)
 constexpr int kFwVec = kFwTok * kFwKC / 8 / kFwThreads;   // staged 8-element vectors per thread
@@ -398,16 +402,20 @@ moe_fc_wide(const _Float16* __restrict__ act, const int32_t* __restrict__ plists
   // staging: vector i of a thread = token slot (tid + 512 i) / 16 = 32 i +
   // tid / 16 (token tile i), 8 k at 8 (tid % 16); only the pass's token
   // tiles are staged
-  v8h stg[2][kFwVec];
+  v8h stg[kFwWBuf][kFwVec];
   const int kq = tid % (kFwKC / 8);
   int64_t abase[kFwVec];     // element offset of the slot's activation row
   bool sval[kFwVec];
-  auto stage_load = [&](int c, v8h (&dst)[kFwVec], int ntt) __attribute__((always_inline)) {
+  // All kFwVec loads are issued whatever the pass's token count (slots past
+  // it read a valid row and are never stored), so every step issues the same
+  // number of loads and the compiler's load-counter waits stay exact; with a
+  // count-dependent number of loads it waits conservatively, for loads issued
+  // only one step earlier.
+  auto stage_load = [&](int c, v8h (&dst)[kFwVec]) __attribute__((always_inline)) {
     const int k0 = c * kFwKC + 8 * kq;
     const int k = k0 < K ? k0 : 8 * kq;
 #pragma unroll
-    for (int i = 0; i < kFwVec; ++i)
-      if (i < ntt) dst[i] = *reinterpret_cast<const v8h*>(act + abase[i] + k);
+    for (int i = 0; i < kFwVec; ++i) dst[i] = *reinterpret_cast<const v8h*>(act + abase[i] + k);
   };
   auto stage_store = [&](int c, const v8h (&src)[kFwVec], _Float16* xb, int ntt) __attribute__((always_inline)) {
     const bool kv = c * kFwKC + 8 * kq < K;
@@ -437,15 +445,22 @@ moe_fc_wide(const _Float16* __restrict__ act, const int32_t* __restrict__ plists
     s16[1] = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)d.sc, 1);
     s16[2] = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)d.sc, 2);
     s16[3] = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)d.sc, 3);
+    // the chunk's eight weight fragments once, then per token tile its eight
+    // activation fragments read together before its eight MFMAs (one LDS
+    // round trip per tile rather than per MFMA; each accumulator still sums
+    // its fragments in the order m = 0..7)
+    v8h af[8];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const v8h af = dequant8_w(kv ? words[m] : 0u, s16[m >> 1]);
+    for (int m = 0; m < 8; ++m) af[m] = dequant8_w(kv ? words[m] : 0u, s16[m >> 1]);
 #pragma unroll
-      for (int tt = 0; tt < kFwTT; ++tt) {
-        if (tt >= ntt) break;   // wave-uniform
-        const v8h bf = *reinterpret_cast<const v8h*>(xb + (32 * tt + r32) * kFwPitch + 64 * h + 8 * m);
-        acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf, acc[tt], 0, 0, 0);
-      }
+    for (int tt = 0; tt < kFwTT; ++tt) {
+      if (tt >= ntt) break;   // wave-uniform
+      v8h bf[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        bf[m] = *reinterpret_cast<const v8h*>(xb + (32 * tt + r32) * kFwPitch + 64 * h + 8 * m);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[m], bf[m], acc[tt], 0, 0, 0);
     }
   };
 
@@ -555,8 +570,9 @@ moe_fc_wide(const _Float16* __restrict__ act, const int32_t* __restrict__ plists
       sval[i] = slot < ntok;
       abase[i] = (int64_t)srow[slot] * K;
     }
-    stage_load(0, stg[0], ntt);
-    stage_load(1, stg[1], ntt);
+    stage_load(0, stg[0]);
+    stage_load(1, stg[1]);
+    stage_load(2, stg[2]);
     if constexpr (FC == 2) {
       // each slot's exponent e and the factors of its fc1 row tiles
       // (d = et - e <= 0; d > 0 only for an all-zero tile; factors below
@@ -574,21 +590,21 @@ moe_fc_wide(const _Float16* __restrict__ act, const int32_t* __restrict__ plists
     }
     stage_store(0, stg[0], xs[0], ntt);
     lds_barrier();
-    // chunk c of a tile uses weight buffer c % 4, staging registers and LDS
-    // buffer c % 2 (nchp is a multiple of four, so this holds across tiles).
-    // Step c loads the activations of chunk c + 2 and the weights of chunk
-    // c + 3, past the tile's end those of the next tile (of this one past
-    // the last: re-read, unused).
+    // chunk c of a tile uses weight and staging register buffers c % 4 and
+    // LDS buffer c % 2 (nchp is a multiple of four, so this holds across
+    // tiles).  Step c loads the activations and the weights of chunk c + 3,
+    // past the tile's end those of the next tile (of this one past the last:
+    // re-read, unused), so both have two steps of other work before use.
     for (int ti = 0; ti < ntile; ++ti) {
       const uint8_t *wn, *sn;
       wrow(ti + 1 < ntile ? ti + 1 : ti, wn, sn);
       auto step = [&](int c, auto jc) __attribute__((always_inline)) {
         constexpr int j = decltype(jc)::value;
-        stage_load(c + 2 < nchp ? c + 2 : c + 2 - nchp, stg[j & 1], ntt);
+        stage_load(c + 3 < nchp ? c + 3 : c + 3 - nchp, stg[(j + 3) % kFwWBuf]);
         const bool nx = c + 3 >= nchp;
         load_w(nx ? wn : wr, nx ? sn : sr, nx ? c + 3 - nchp : c + 3, wb[(j + 3) % kFwWBuf]);
         compute(c, xs[j & 1], wb[j], ntt);
-        stage_store(c + 1 < nchp ? c + 1 : 0, stg[(j + 1) & 1], xs[(j + 1) & 1], ntt);
+        stage_store(c + 1 < nchp ? c + 1 : 0, stg[(j + 1) % kFwWBuf], xs[(j + 1) & 1], ntt);
         lds_barrier();
       };
       for (int c = 0; c < nchp; c += kFwWBuf) {
