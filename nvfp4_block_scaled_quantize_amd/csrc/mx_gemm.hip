@@ -33,37 +33,13 @@
 
 #include "device_common.h"
 #include "internal.h"
+#include "lds_dma.h"
 
 namespace nvfp4 {
 
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt[3:0] | expcnt[6:4]=7 | lgkmcnt[11:8]=15 | vmcnt[5:4] in bits [15:14]).
-template <int N>
-__device__ __forceinline__ void mx_wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 0xF) | ((N >> 4) << 14));
-}
-
-__device__ __forceinline__ uint32_t mx_lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
-}
-
-// Direct global -> LDS copies: lane i's 16 (4) bytes land at lds + 16*i (4*i).
-// Inline assembly, so that the compiler does not make every later LDS read
-// wait for all outstanding vector-memory operations; the kernel waits for the
-// copies itself (s_waitcnt vmcnt + s_barrier) before reading a stage.
-__device__ __forceinline__ void mx_dma16(const void* sbase, uint32_t vofs, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(lds), "v"(vofs), "s"(sbase) : "memory", "m0");
-}
-__device__ __forceinline__ void mx_dma4(const void* sbase, uint32_t vofs, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
-               :: "s"(lds), "v"(vofs), "s"(sbase) : "memory", "m0");
-}
 
 __device__ __forceinline__ v8i fp4_operand(u32x4 v) {
   v8i r = {(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
@@ -155,18 +131,18 @@ mx_gemm_wide(const uint8_t* __restrict__ a, const uint8_t* __restrict__ as,
   // copy instructions [lo, hi) of stage st (0-3 weight codes, 4-7 activation
   // codes, 8 weight scales, 9 activation scales) into buffer buf
   auto issue_part = [&](unsigned char* buf, int st, int lo, int hi) __attribute__((always_inline)) {
-    const uint32_t l0 = mx_lds_addr(buf);
+    const uint32_t l0 = lds_addr(buf);
 #pragma unroll
     for (int idx = 0; idx < kMwLoads; ++idx) {
       if (idx < lo || idx >= hi) continue;
       if (idx < 4)
-        mx_dma16(wbase + (size_t)st * 2048, wofs[idx], l0 + kMwWOff + (4 * wave + idx) * 1024);
+        dma16(wbase + (size_t)st * 2048, wofs[idx], l0 + kMwWOff + (4 * wave + idx) * 1024);
       else if (idx < 8)
-        mx_dma16(abase + (size_t)st * 2048, aofs[idx - 4], l0 + kMwAOff + (4 * wave + idx - 4) * 1024);
+        dma16(abase + (size_t)st * 2048, aofs[idx - 4], l0 + kMwAOff + (4 * wave + idx - 4) * 1024);
       else if (idx == 8)
-        mx_dma4(wsbase + (size_t)st * 128, wsofs, l0 + kMwWSOff + wave * 256);
+        dma4(wsbase + (size_t)st * 128, wsofs, l0 + kMwWSOff + wave * 256);
       else
-        mx_dma4(asbase + (size_t)st * 128, asofs, l0 + kMwASOff + wave * 256);
+        dma4(asbase + (size_t)st * 128, asofs, l0 + kMwASOff + wave * 256);
     }
   };
   auto issue = [&](unsigned char* buf, int st) __attribute__((always_inline)) {
@@ -271,8 +247,8 @@ mx_gemm_wide(const uint8_t* __restrict__ a, const uint8_t* __restrict__ as,
     }
     __builtin_amdgcn_sched_barrier(0);
     if (s + 1 < nstages) {
-      if (s + 2 < nstages) mx_wait_vmcnt<kMwLoads>();
-      else mx_wait_vmcnt<0>();
+      if (s + 2 < nstages) wait_vmcnt_le<kMwLoads>();
+      else wait_vmcnt_le<0>();
       __builtin_amdgcn_s_barrier();
       read_scales(next1, c0n);
       read_frags(next1, 0, f0n);
@@ -285,9 +261,9 @@ mx_gemm_wide(const uint8_t* __restrict__ a, const uint8_t* __restrict__ as,
   issue(lds0, 0);
   if (nstages > 1) issue(lds1, 1);
   if (nstages > 2) issue(lds2, 2);
-  if (nstages > 2) mx_wait_vmcnt<2 * kMwLoads>();
-  else if (nstages > 1) mx_wait_vmcnt<kMwLoads>();
-  else mx_wait_vmcnt<0>();
+  if (nstages > 2) wait_vmcnt_le<2 * kMwLoads>();
+  else if (nstages > 1) wait_vmcnt_le<kMwLoads>();
+  else wait_vmcnt_le<0>();
   __builtin_amdgcn_s_barrier();
   Frags fa, fb;
   Scales ca, cb;
