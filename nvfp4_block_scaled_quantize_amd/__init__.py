@@ -343,6 +343,11 @@ def mx_gemm(a: dict, a_g: torch.Tensor, w: dict, w_g: torch.Tensor, a_group_rows
     B, N, K = a["rows"], w["rows"], a["K"]
     if w["K"] != K:
         raise ValueError("operand K differs")
+    for op, r in ((a, B), (w, N)):
+        nc, ns = mx_tiled_sizes(r, K)
+        if op["codes"].dtype != torch.uint8 or op["sf"].dtype != torch.uint8 or \
+                op["codes"].numel() < nc or op["sf"].numel() < ns:
+            raise ValueError("tile buffers smaller than the MX tile layout of %d x %d" % (r, K))
     if a_g.dtype != torch.float32 or w_g.dtype != torch.float32:
         raise TypeError("globals must be float32")
     y = out if out is not None else torch.empty((B, N), dtype=torch.float16, device=a["codes"].device)

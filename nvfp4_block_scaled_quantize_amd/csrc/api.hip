@@ -165,7 +165,8 @@ int32_t nvfp4_mx_tile(const uint8_t* codes, const uint8_t* sf, int64_t rows, int
   if (((uintptr_t)codes % 16) != 0 || ((uintptr_t)codes_tiled % 16) != 0 ||
       ((uintptr_t)sf_tiled % 2) != 0)
     return NVFP4_EINVAL;
-  if (k > (1LL << 24) || (rows + 31) / 32 * (k / 64) > (1LL << 33)) return NVFP4_EUNSUPPORTED;
+  // four 1 KiB tiles per workgroup of the permutation: grid.x < 2^31
+  if (k > (1LL << 24) || (rows + 31) / 32 * (k / 64) > (1LL << 32)) return NVFP4_EUNSUPPORTED;
   const int32_t ds = device_status();
   if (ds != NVFP4_OK) return ds;
   return hip_status(nvfp4::launch_mx_tile(codes, sf, rows, k, codes_tiled, sf_tiled,
