@@ -73,6 +73,19 @@ def test_quantize_per_tensor_and_per_expert(nv, oracle, group):
         _eq(key, got[key], want[key])
 
 
+@pytest.mark.parametrize("rows,k,gr", [(300, 1024, 300), (96, 384, 24), (40, 8192, 40)])
+def test_quantize_tiled_grouped_globals(nv, oracle, rows, k, gr):
+    """Per-tensor / per-expert globals straight into the tile layout (the weight
+    preparation of the MX benchmark), ragged row counts included."""
+    x = torch.from_numpy(si.normal_f32((rows, k), 0.02, 97, 2, seed=rows + gr)).to(torch.bfloat16)
+    want = oracle.mx_quantize(x, group_rows=gr)
+    ct, st = oracle.mx_tile(want["codes"], want["sf"])
+    got = _gpu_mxq(nv, x, group_rows=gr, tiled=True)
+    _eq("codes", got["codes"], ct)
+    _eq("sf", got["sf"], st)
+    _eq("g_dec", got["g_dec"], want["g_dec"])
+
+
 @pytest.mark.parametrize("act", ["none", "swiglu"])
 @pytest.mark.parametrize("rows,k", [(1, 128), (45, 128), (64, 384), (300, 1024), (33, 8192)])
 def test_quantize_tiled_bit_exact(nv, oracle, act, rows, k):
