@@ -53,7 +53,7 @@ def _gpu_quant(nv, x, act, group_rows=1):
 @pytest.mark.parametrize("act", ["none", "swiglu", "relu2"])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("rows,k_out", [(1, 16), (3, 32), (37, 48), (5, 256), (9, 1040), (4, 4096),
-                                         (2, 14336), (3, 32784)])
+                                         (2, 14336), (1, 32768), (3, 32784)])
 def test_small_shapes_bit_exact(nv, oracle, act, dtype, rows, k_out):
     k_in = 2 * k_out if act == "swiglu" else k_out
     x32 = si.normal_f32((rows, k_in), 1.0, 90, 0, seed=rows * 7 + k_out,
