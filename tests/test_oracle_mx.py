@@ -155,6 +155,30 @@ def test_on_grid_round_trip(oracle):
     assert not deq[:, 1:32].any()
 
 
+def test_zero_block_inside_a_row_keeps_signed_zero_codes(oracle):
+    """An all-zero block (alternating -0 / +0) next to a block with maximum 3:
+    g_dec = 3/2688, the zero block's scale is the smallest E8M0 value (byte 0,
+    2^-127), its combined scale 2^-127 * 3/2688 is a binary32 subnormal, so the
+    encode factor 1/c overflows to +inf -- and every zero element must still get
+    the zero code with its own sign (reading of the NVFP4 zero rule, kept for MX),
+    not the code of 0 * inf."""
+    x = np.zeros((1, 64), np.float32)
+    x[0, 0:32:4] = -0.0            # -0 and +0 in both nibble positions of the bytes
+    x[0, 3:32:4] = -0.0
+    x[0, 32:] = np.linspace(-3.0, 3.0, 32)
+    xt = torch.from_numpy(x).to(torch.bfloat16)
+    assert xt[0, 0].item() == 0.0 and math.copysign(1.0, xt[0, 0].item()) < 0
+    q = oracle.mx_quantize(xt)
+    assert q["sf"][0, 0] == 0
+    c0 = np.float32(oracle.e8m0_decode(0)) * np.float32(q["g_dec"][0])
+    assert 0.0 < c0 < np.finfo(np.float32).tiny
+    with np.errstate(over="ignore"):
+        assert np.isinf(np.float32(1.0) / c0)
+    want = np.where(np.signbit(x[0, :32]), 8, 0).astype(np.uint8)
+    codes = q["codes"][0, :16]
+    assert np.array_equal(codes & 0xF, want[0::2]) and np.array_equal(codes >> 4, want[1::2])
+
+
 def test_group_scale_per_tensor_equals_per_row_when_maxima_match(oracle):
     rng = np.random.default_rng(5)
     x = rng.standard_normal((4, 128)).astype(np.float32)
