@@ -81,6 +81,7 @@ def test_edge_rows(nv, oracle):
     x[1] = 3.0                                    # constant row
     x[2] = -0.0                                   # negative zeros
     x[3, 5] = 7.5                                 # single non-zero
+    x[3, 16:32:3] = -0.0                          # signed zeros in an all-zero block of that row
     x[4] = torch.tensor(np.full(k, 1e-39, np.float32)).to(torch.bfloat16)   # subnormal bf16
     x[5, :16] = torch.tensor(np.linspace(-1e-38, 1e-38, 16, dtype=np.float32)).to(torch.bfloat16)
     x[6] = torch.tensor(np.geomspace(1e-30, 1e30, k, dtype=np.float32)).to(torch.bfloat16)
