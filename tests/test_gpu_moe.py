@@ -64,7 +64,7 @@ def _check(oracle, nv, c, top_k, n_group, topk_group, norm=True, scaling=1.0, to
                          [(5, 8, 2, 2, 1, 64, 128), (32, 16, 4, 4, 2, 256, 128), (70, 64, 8, 8, 4, 128, 64),
                           (300, 32, 6, 4, 3, 192, 320), (3, 256, 16, 16, 4, 64, 64),
                           (600, 8, 4, 2, 2, 64, 64), (200, 8, 2, 2, 2, 448, 320),
-                          (1500, 4, 1, 1, 1, 576, 128)])
+                          (1500, 4, 1, 1, 1, 576, 128), (1, 8, 2, 2, 1, 64, 64), (8, 4, 2, 1, 1, 64, 8192)])
 def test_small_layers(nv, oracle, T, E, top_k, n_group, topk_group, hidden, inter):
     c = _case(oracle, T, E, hidden, inter, seed=T + E)
     _check(oracle, nv, c, top_k, n_group, topk_group)
