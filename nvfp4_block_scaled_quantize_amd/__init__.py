@@ -117,6 +117,12 @@ def _workspace(nbytes: int, device, workspace: torch.Tensor | None):
     return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
 
 
+def quantize_workspace_size(rows: int, k: int, group_rows: int) -> int:
+    """Bytes of caller workspace that quantize() / mx_quantize() need for one
+    global per `group_rows` rows (0 for per-token globals)."""
+    return int(_lib.nvfp4_quantize_workspace_size(rows, k, group_rows))
+
+
 def quantize(x: torch.Tensor, group_rows: int = 1, want_scale: bool = True, out: dict | None = None,
              workspace: torch.Tensor | None = None, stream=None) -> dict:
     """NVFP4-quantize x [rows, k] with one global scale per `group_rows` rows."""

@@ -71,7 +71,7 @@ def test_graph_replays_match_eager(nv):
     outs["mxa"] = {"codes": torch.empty(nc, dtype=torch.uint8, device=dev),
                    "sf": torch.empty(ns, dtype=torch.uint8, device=dev),
                    "g_dec": torch.empty((256,), dtype=torch.float32, device=dev)}
-    wsq = torch.empty(max(nv._lib.nvfp4_quantize_workspace_size(512, 512, 512), 256), dtype=torch.uint8,
+    wsq = torch.empty(max(nv.quantize_workspace_size(512, 512, 512), 256), dtype=torch.uint8,
                       device=dev)
     wsg = torch.empty(max(nv.gemm_workspace_size(256, 512, 512), 256), dtype=torch.uint8, device=dev)
     wsm = torch.empty(nv.moe_workspace_size(T, E, topk, Hd, I), dtype=torch.uint8, device=dev)
