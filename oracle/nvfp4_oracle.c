@@ -163,6 +163,7 @@ uint8_t oracle_e2m1_encode(float v) {
 static float f32_of(double d) { return (float)d; }
 
 float oracle_exp(float x) {
+  if (x != x) return x;                           /* NaN propagates (the reduction needs a number) */
   if (x > 88.75f) return INFINITY;
   if (x < -87.0f) return 0.0f;
   const double ln2 = 0.693147180559945309417232121458176568;
