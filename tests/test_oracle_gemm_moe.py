@@ -176,6 +176,54 @@ def test_moe_ref_closed_form(oracle):
     assert np.allclose(out2, xr * 4.0 * 3.0, rtol=1e-14)
 
 
+def _select_weight(N, K, src, sf_byte):
+    """Weights [N, K] whose row n holds code 2 (= 1.0) at column src[n] and
+    zeros elsewhere, every block scale the E4M3 byte sf_byte."""
+    nib = np.zeros((N, K), np.uint8)
+    nib[np.arange(N), src] = 2
+    codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    return codes, np.full((N, K // 16), sf_byte, np.uint8)
+
+
+def test_moe_ref_distinct_experts_closed_form(oracle):
+    # Every expert is a different selection: fc1_e row i picks x[p_e(i)]
+    # (inter != hidden, so a transposed operand cannot even be formed), fc2_e
+    # row n picks h[q_e(n)]; expert e has its own power-of-two globals g1[e],
+    # g2[e] and its own E4M3 block scale s1[e], s2[e]; routing weights differ
+    # per token and rank, and x has negative entries.  Then exactly
+    #   out_t[n] = sum_j w_tj * g2[e] s2[e] * (g1[e] s1[e])^2 * relu(x_t[p_e(q_e(n))])^2
+    # with e = ids[t, j] ("Nvfp4 A16 Blackwell Moe Runner": per-expert
+    # globalScales, ReLU2, normalised top-k weights applied per rank).
+    rng = np.random.default_rng(44)
+    T, E, top_k, H, I = 7, 5, 3, 32, 48
+    x = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).half()
+    p = [rng.integers(0, H, I) for _ in range(E)]          # fc1 row i <- x[p_e(i)]
+    q = [rng.permutation(I)[:H] for _ in range(E)]         # fc2 row n <- h[q_e(n)]
+    e4m3 = {0x30: 0.5, 0x38: 1.0, 0x40: 2.0, 0x48: 4.0}
+    s1b = [0x38, 0x40, 0x30, 0x48, 0x38]
+    s2b = [0x40, 0x38, 0x48, 0x30, 0x30]
+    g1 = np.array([1.0, 0.5, 2.0, 0.25, 4.0], np.float32)
+    g2 = np.array([2.0, 0.125, 1.0, 8.0, 0.5], np.float32)
+    w1 = [_select_weight(I, H, p[e], s1b[e]) for e in range(E)]
+    w2 = [_select_weight(H, I, q[e], s2b[e]) for e in range(E)]
+    w1c = np.stack([c for c, _ in w1]); w1s = np.stack([s for _, s in w1])
+    w2c = np.stack([c for c, _ in w2]); w2s = np.stack([s for _, s in w2])
+    ids = np.stack([rng.permutation(E)[:top_k] for _ in range(T)]).astype(np.int32)
+    wts = rng.uniform(0.1, 1.0, (T, top_k)).astype(np.float32)
+    out = oracle.moe_ref(x.numpy(), ids, wts, w1c, w1s, g1, w2c, w2s, g2)
+    xd = x.double().numpy()
+    want = np.zeros((T, H))
+    for t in range(T):
+        for j in range(top_k):
+            e = int(ids[t, j])
+            f = float(g2[e]) * e4m3[s2b[e]] * (float(g1[e]) * e4m3[s1b[e]]) ** 2
+            want[t] += float(wts[t, j]) * f * np.maximum(xd[t, p[e][q[e]]], 0.0) ** 2
+    assert np.allclose(out, want, rtol=1e-13, atol=0.0)
+    # `tokens` selects rows of the same result
+    sub = oracle.moe_ref(x.numpy(), ids, wts, w1c, w1s, g1, w2c, w2s, g2, tokens=[5, 0, 3])
+    assert np.array_equal(sub, out[[5, 0, 3]])
+
+
 # ---------------------------------------------------------------- pre-tiled weights
 
 def test_pretile_worked_positions(oracle):
