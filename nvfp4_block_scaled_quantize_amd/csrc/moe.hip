@@ -211,7 +211,9 @@ moe_lists(const int32_t* __restrict__ ids, int P, int T, int top_k, int32_t* __r
   int32_t* tl = tlists + (int64_t)e * T;
   const uint64_t lt = (1ull << lane) - 1ull;
   int cnt = 0;
-  if (c1 - c0 <= kListRegs) {
+  // the branch depends on `per` only (block-uniform), so every wave reaches
+  // the same barrier; each wave's share c1 - c0 is at most `per`
+  if (per <= kListRegs) {
     uint64_t masks[kListRegs];
     int v[kListRegs];
 #pragma unroll
