@@ -121,10 +121,17 @@ int32_t nvfp4_act_quant(const void* x, int32_t dtype, int64_t rows, int64_t k_ou
  *   w_sf     : [N, K/16] uint8 E4M3 weight block scales
  *   w_gscale : pointer to ONE float on the device, the global weight scale
  *   y        : [B, N] fp16 out (round-to-nearest-even from fp32 accumulation)
- *   workspace: nvfp4_gemm_workspace_size() bytes (may be 0 -> NULL allowed)
- * Requires B >= 0, N > 0, K > 0, K % 32 == 0 (whole bytes of 16-blocks in
- * pairs); w 16-byte aligned, w_sf 2-byte aligned, a_scale and w_gscale
- * 4-byte aligned (EINVAL otherwise).  B == 0 is a no-op.
+ *   workspace: nvfp4_gemm_workspace_size() bytes, 256-byte aligned (the size
+ *              may be 0 -> NULL allowed); EWORKSPACE if smaller or misaligned
+ * Requires B >= 0, N > 0, K > 0, K % 16 == 0 (whole 16-blocks, the [N, K/16]
+ * block scale of the plugin contract); a_scale and w_gscale 4-byte aligned,
+ * y 2-byte aligned (EINVAL otherwise).  w and w_sf may have any alignment:
+ * weights whose rows are not 16-byte aligned (w not 16-byte aligned, w_sf
+ * not 2-byte aligned, or K % 32 == 16) take a byte-load path with the same
+ * arithmetic, so its results are bit-identical to those of the aligned path
+ * on the same values ("Building Custom TensorRT-LLM Plugins for Low-Latency
+ * FP8 Inference at Scale", "Production Pitfalls & Hard Lessons", item 1).
+ * B == 0 is a no-op.
  */
 int32_t nvfp4_gemm(const uint8_t* a, const float* a_scale, const uint8_t* w, const uint8_t* w_sf,
                    const float* w_gscale, void* y, int64_t B, int64_t N, int64_t K,
@@ -156,8 +163,8 @@ int32_t nvfp4_pretile_weight(const uint8_t* w, const uint8_t* w_sf, int64_t N, i
  * nvfp4_gemm_pretiled -- nvfp4_gemm with the weight operands in the
  * pre-tiled layout.  Same arithmetic and results as nvfp4_gemm on the
  * untiled weights (bit-identical output), same workspace
- * (nvfp4_gemm_workspace_size).  Requires N % 16 == 0, K % 128 == 0,
- * K <= 2^24, w_tiled 16-byte and sf_tiled 4-byte aligned.
+ * (nvfp4_gemm_workspace_size, 256-byte aligned).  Requires N % 16 == 0,
+ * K % 128 == 0, K <= 2^24, w_tiled 16-byte and sf_tiled 4-byte aligned.
  */
 int32_t nvfp4_gemm_pretiled(const uint8_t* a, const float* a_scale, const uint8_t* w_tiled,
                             const uint8_t* sf_tiled, const float* w_gscale, void* y, int64_t B,
@@ -175,10 +182,10 @@ int32_t nvfp4_gemm_pretiled(const uint8_t* a, const float* a_scale, const uint8_
  * out_features = N, in_features = K, scale_cols = K/16).  Host-only: no HIP
  * call, no copy; the pointers must stay valid for every GEMM that uses the
  * resource, and the caller unregisters before releasing the storage.
- *   weight : [N, K/2] uint8 device codes, 16-byte aligned
- *   scale  : [N, K/16] uint8 device E4M3 bytes, 2-byte aligned
+ *   weight : [N, K/2] uint8 device codes (any alignment, as for nvfp4_gemm)
+ *   scale  : [N, K/16] uint8 device E4M3 bytes
  * Requires device >= 0, resource_id >= 0 (a negative id means baked-weight
- * mode in the plugin and is rejected here), N > 0, K > 0, K % 32 == 0,
+ * mode in the plugin and is rejected here), N > 0, K > 0, K % 16 == 0,
  * scale_cols == K/16, and (device, resource_id) not registered yet; EINVAL
  * otherwise (the registry is unchanged on error).
  */

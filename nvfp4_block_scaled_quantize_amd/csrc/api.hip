@@ -43,6 +43,7 @@ int32_t device_status() {
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP; }
 
 bool aligned4(const void* p) { return ((uintptr_t)p % 4) == 0; }
+bool aligned256(const void* p) { return ((uintptr_t)p % 256) == 0; }
 
 // External weights of "Fused Nvfp4 GEMM All Reduce Plugin" (external-weight
 // mode): (device, resource id) -> the caller's weight and scale pointers.
@@ -206,14 +207,14 @@ size_t nvfp4_gemm_workspace_size(int64_t B, int64_t N, int64_t K) {
 int32_t nvfp4_gemm(const uint8_t* a, const float* a_scale, const uint8_t* w, const uint8_t* w_sf,
                    const float* w_gscale, void* y, int64_t B, int64_t N, int64_t K,
                    void* workspace, size_t workspace_bytes, void* stream) {
-  if (B < 0 || N <= 0 || K <= 0 || (K % 32) != 0) return NVFP4_EINVAL;
+  if (B < 0 || N <= 0 || K <= 0 || (K % 16) != 0) return NVFP4_EINVAL;
   if (B == 0) return NVFP4_OK;
   if (!a || !a_scale || !w || !w_sf || !w_gscale || !y) return NVFP4_EINVAL;
   if (!aligned4(a_scale) || !aligned4(w_gscale) || ((uintptr_t)y % 2) != 0) return NVFP4_EINVAL;
-  if (((uintptr_t)w % 16) != 0 || ((uintptr_t)w_sf % 2) != 0) return NVFP4_EINVAL;
   if (B > 0x7FFFFFFFLL || N > 0x7FFFFFFFLL || K > 0x7FFFFFFFLL) return NVFP4_EUNSUPPORTED;
   const size_t need = nvfp4::gemm_workspace_bytes(B, N, K);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return NVFP4_EWORKSPACE;
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned256(workspace)))
+    return NVFP4_EWORKSPACE;
   const int32_t ds = device_status();
   if (ds != NVFP4_OK) return ds;
   nvfp4::GemmArgs g{a, a_scale, w, w_sf, w_gscale, y, B, N, K, workspace, workspace_bytes, 0};
@@ -244,7 +245,8 @@ int32_t nvfp4_gemm_pretiled(const uint8_t* a, const float* a_scale, const uint8_
   if (((uintptr_t)w_tiled % 16) != 0 || ((uintptr_t)sf_tiled % 4) != 0) return NVFP4_EINVAL;
   if (B > 0x7FFFFFFFLL || N > 0x7FFFFFFFLL || K > (1LL << 24)) return NVFP4_EUNSUPPORTED;
   const size_t need = nvfp4::gemm_workspace_bytes(B, N, K);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return NVFP4_EWORKSPACE;
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned256(workspace)))
+    return NVFP4_EWORKSPACE;
   const int32_t ds = device_status();
   if (ds != NVFP4_OK) return ds;
   nvfp4::GemmArgs g{a, a_scale, w_tiled, sf_tiled, w_gscale, y, B, N, K, workspace, workspace_bytes, 1};
@@ -255,10 +257,9 @@ int32_t nvfp4_register_weight(int32_t device, int32_t resource_id, const uint8_t
                               const uint8_t* scale, int32_t out_features, int32_t in_features,
                               int32_t scale_cols) {
   if (device < 0 || resource_id < 0 || !weight || !scale) return NVFP4_EINVAL;
-  if (out_features <= 0 || in_features <= 0 || (in_features % 32) != 0 ||
+  if (out_features <= 0 || in_features <= 0 || (in_features % 16) != 0 ||
       scale_cols != in_features / 16)
     return NVFP4_EINVAL;
-  if (((uintptr_t)weight % 16) != 0 || ((uintptr_t)scale % 2) != 0) return NVFP4_EINVAL;
   Registry& r = registry();
   std::lock_guard<std::mutex> lock(r.mu);
   const bool inserted =
@@ -324,8 +325,7 @@ int32_t nvfp4_moe_w4a16(const float* router_logits, const float* correction_bias
       !aligned4(router_logits) || !aligned4(correction_bias) || !aligned4(w1_g) || !aligned4(w2_g))
     return NVFP4_EINVAL;
   const size_t need = nvfp4::moe_workspace_bytes(tokens, experts, top_k, hidden, inter);
-  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % 256) != 0)
-    return NVFP4_EWORKSPACE;
+  if (!workspace || workspace_bytes < need || !aligned256(workspace)) return NVFP4_EWORKSPACE;
   const int32_t ds = device_status();
   if (ds != NVFP4_OK) return ds;
   nvfp4::MoeArgs m{router_logits, correction_bias, x, w1, w1_sf, w1_g, w2, w2_sf, w2_g, out,

@@ -92,6 +92,23 @@ __device__ __forceinline__ uint32_t load_u32_bytes(const uint8_t* p) {
   return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
 }
 
+// The 32 codes (16 bytes) of a row at byte p by byte loads, any alignment;
+// when only the first 16 of the 32 k are inside the row (K % 32 == 16 at
+// the row end), the upper 8 bytes are zero and are not read.
+__device__ __forceinline__ uint4 load_codes32_bytes(const uint8_t* p, bool full) {
+  uint4 r;
+  r.x = load_u32_bytes(p);
+  r.y = load_u32_bytes(p + 4);
+  r.z = full ? load_u32_bytes(p + 8) : 0u;
+  r.w = full ? load_u32_bytes(p + 12) : 0u;
+  return r;
+}
+
+// Weight operand layouts of the GEMM kernels.
+constexpr int kWPlain = 0;   // [N, K/2] codes, 16-byte aligned rows (K % 32 == 0)
+constexpr int kWTiled = 1;   // the pre-tiled layout
+constexpr int kWBytes = 2;   // [N, K/2] codes at any alignment, K % 16 == 0 (byte loads)
+
 // ------------------------------------------------------------ skinny (decode)
 
 constexpr int kSkThreads = 512;   // 8 waves
@@ -119,10 +136,13 @@ constexpr size_t kSkRedBytes = (size_t)kSkKs * kSkRows * 16 * sizeof(float);
 //  4. the four K quarters are summed in LDS in a fixed order.
 // A4: activation codes 4-byte aligned (dword loads), else byte loads.
 // NI: activation items (units of eight codes) per thread, >= B * ceil(K/8 / 512).
-// TILED: the weights are in the pre-tiled layout (nvfp4_pretile_weight): each
-// wave-load of 16 rows x 128 k is one contiguous KiB (codes) / 128 B (E4M3
-// bytes) instead of 16 row segments.
-template <bool A4, int NI, bool TILED>
+// WL = kWTiled: the weights are in the pre-tiled layout (nvfp4_pretile_weight):
+// each wave-load of 16 rows x 128 k is one contiguous KiB (codes) / 128 B (E4M3
+// bytes) instead of 16 row segments.  WL = kWBytes: the scalar path for
+// weights at any alignment and K % 16 == 0: the same arithmetic on the same
+// values (bit-identical results), with byte loads, and both operands zeroed
+// for the k past the row end of a half-filled last 32-k group.
+template <bool A4, int NI, int WL>
 __global__ void __launch_bounds__(kSkThreads)
 gemm_skinny(const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
             const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_sf,
@@ -178,11 +198,17 @@ gemm_skinny(const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
     for (int i = 0; i < kSkPF; ++i) {
       if (i < i0 || i >= i1) continue;
       const int c = c0 + i * kSkKs;
-      if constexpr (TILED) {
+      if constexpr (WL == kWTiled) {
         // tile (row group, chunk), lane order r16 + 16 g (K % 128 == 0)
         const int64_t t = ((int64_t)(nrow < N ? nrow : N - 1) / 16 * nchunks + (c < nchunks ? c : 0)) * 64 + lane;
         wc[i] = *reinterpret_cast<const uint4*>(w + t * 16);
         wsv[i] = (uint32_t)*reinterpret_cast<const uint16_t*>(w_sf + t * 2);
+      } else if constexpr (WL == kWBytes) {
+        const int k0 = c * 128 + 32 * g;
+        const int k = (c < nchunks && k0 < K) ? k0 : 0;
+        const bool full = k + 16 < K;
+        wc[i] = load_codes32_bytes(wr + k / 2, full);
+        wsv[i] = (uint32_t)sr[k / 16] | (full ? (uint32_t)sr[k / 16 + 1] << 8 : 0u);
       } else {
         const int k0 = c * 128 + 32 * g;
         const int k = (c < nchunks && k0 < K) ? k0 : 0;
@@ -247,6 +273,10 @@ gemm_skinny(const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
         v8h bf[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) bf[m] = *reinterpret_cast<const v8h*>(arow + (kv ? k : 0) + 8 * m);
+        if constexpr (WL == kWBytes) {
+          // k + 16 .. k + 31 past the row end: the LDS there is not this row
+          if (k + 16 >= K) { bf[2] = v8h{}; bf[3] = v8h{}; }
+        }
         const _Float16 s0 = e4m3_b0_f16(wsv[i]), s1 = e4m3_b1_f16(wsv[i]);
         const uint32_t cw[4] = {kv ? wc[i].x : 0u, kv ? wc[i].y : 0u, kv ? wc[i].z : 0u, kv ? wc[i].w : 0u};
 #pragma unroll
@@ -283,17 +313,19 @@ typedef void (*SkinnyFn)(const uint8_t*, const float*, const uint8_t*, const uin
                          _Float16*, int, int, int);
 
 // The instantiation with the fewest activation items per thread covering ni.
-template <bool A4, bool TILED>
+template <bool A4, int WL>
 SkinnyFn skinny_kernel_a(int ni) {
-  if (ni <= 1) return gemm_skinny<A4, 1, TILED>;
-  if (ni <= 2) return gemm_skinny<A4, 2, TILED>;
-  if (ni <= 4) return gemm_skinny<A4, 4, TILED>;
-  if (ni <= 8) return gemm_skinny<A4, 8, TILED>;
-  return gemm_skinny<A4, kSkItems, TILED>;
+  if (ni <= 1) return gemm_skinny<A4, 1, WL>;
+  if (ni <= 2) return gemm_skinny<A4, 2, WL>;
+  if (ni <= 4) return gemm_skinny<A4, 4, WL>;
+  if (ni <= 8) return gemm_skinny<A4, 8, WL>;
+  return gemm_skinny<A4, kSkItems, WL>;
 }
-SkinnyFn skinny_kernel(bool a4, int ni, bool tiled) {
-  if (tiled) return a4 ? skinny_kernel_a<true, true>(ni) : skinny_kernel_a<false, true>(ni);
-  return a4 ? skinny_kernel_a<true, false>(ni) : skinny_kernel_a<false, false>(ni);
+// The byte-load weight path uses byte loads for the activation codes too.
+SkinnyFn skinny_kernel(bool a4, int ni, int wl) {
+  if (wl == kWBytes) return skinny_kernel_a<false, kWBytes>(ni);
+  if (wl == kWTiled) return a4 ? skinny_kernel_a<true, kWTiled>(ni) : skinny_kernel_a<false, kWTiled>(ni);
+  return a4 ? skinny_kernel_a<true, kWPlain>(ni) : skinny_kernel_a<false, kWPlain>(ni);
 }
 
 size_t skinny_lds_bytes(int64_t B, int64_t K) {
@@ -343,6 +375,10 @@ constexpr size_t kSStage = (size_t)kTN * 4;
 constexpr size_t kStage = kAStage + kWStage + kSStage;
 constexpr size_t kTiledLds = 2 * kStage;
 
+// WB: the weight codes at any alignment and K % 16 == 0 (byte loads; the
+// upper 16 k of a half-filled last 32-k group read as zero codes).  Same
+// products in the same order as gemm_wide, so bit-identical results.
+template <bool WB>
 __global__ void __launch_bounds__(kTThreads)
 gemm_tiled(const _Float16* __restrict__ a16, const float* __restrict__ rowscale,
            const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_sf,
@@ -375,8 +411,12 @@ gemm_tiled(const _Float16* __restrict__ a16, const float* __restrict__ rowscale,
       const int p = tid + kTThreads * i;
       const int row = p >> 1, hh = p & 1;
       const int gn = n0 + row, k = k0 + 32 * hh;
-      rw[i] = (gn < N && k < K) ? *reinterpret_cast<const uint4*>(w + (int64_t)gn * kb2 + k / 2)
-                                : make_uint4(0, 0, 0, 0);
+      if constexpr (WB)
+        rw[i] = (gn < N && k < K) ? load_codes32_bytes(w + (int64_t)gn * kb2 + k / 2, k + 16 < K)
+                                  : make_uint4(0, 0, 0, 0);
+      else
+        rw[i] = (gn < N && k < K) ? *reinterpret_cast<const uint4*>(w + (int64_t)gn * kb2 + k / 2)
+                                  : make_uint4(0, 0, 0, 0);
     }
     {
       const int gn = n0 + tid;
@@ -735,23 +775,29 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, []() {
-    for (int tl = 0; tl < 2 && attr_err == hipSuccess; ++tl)
+    for (int wl = kWPlain; wl <= kWBytes && attr_err == hipSuccess; ++wl)
       for (int a4 = 0; a4 < 2 && attr_err == hipSuccess; ++a4)
         for (int ni = 1; ni <= kSkItems && attr_err == hipSuccess; ni *= 2)
-          attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(skinny_kernel(a4 != 0, ni, tl != 0)),
+          attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(skinny_kernel(a4 != 0, ni, wl)),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSkinnyDynMax);
     if (attr_err == hipSuccess)
-      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled),
+      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled<false>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTiledLds);
+    if (attr_err == hipSuccess)
+      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled<true>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTiledLds);
 
   });
   if (attr_err != hipSuccess) return attr_err;
   const int B = (int)g.B, N = (int)g.N, K = (int)g.K;
   _Float16* y = reinterpret_cast<_Float16*>(g.y);
+  // 16-byte weight rows and 2-byte scale rows, else the byte-load path
+  const bool w_rows16 = ((uintptr_t)g.w % 16) == 0 && (K % 32) == 0 && ((uintptr_t)g.w_sf % 2) == 0;
+  const int wl = g.tiled ? kWTiled : (w_rows16 ? kWPlain : kWBytes);
   if (use_skinny(g.B, g.K)) {
     const unsigned grid = (unsigned)((N + kSkRows - 1) / kSkRows);
     const int ni = B * ((K / 8 + kSkThreads - 1) / kSkThreads);
-    const SkinnyFn fn = skinny_kernel(((uintptr_t)g.a % 4) == 0, ni, g.tiled != 0);
+    const SkinnyFn fn = skinny_kernel(((uintptr_t)g.a % 4) == 0, ni, wl);
     hipLaunchKernelGGL(fn, dim3(grid), dim3(kSkThreads), skinny_lds_bytes(B, K), s, g.a, g.a_scale,
                        g.w, g.w_sf, g.w_g, y, B, N, K);
     return hipGetLastError();
@@ -760,7 +806,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   _Float16* a16 = reinterpret_cast<_Float16*>(ws);
   float* rowscale = reinterpret_cast<float*>(ws + align256((size_t)B * (size_t)K * 2));
   // gemm_wide's copies take 32-bit lane offsets of up to 512 rows x K bytes
-  const bool wide = g.tiled || (K % kTK == 0 && ((uintptr_t)g.w_sf % 4) == 0 && g.K <= (1 << 24));
+  const bool wide = g.tiled || (w_rows16 && K % kTK == 0 && ((uintptr_t)g.w_sf % 4) == 0 && g.K <= (1 << 24));
   hipLaunchKernelGGL(a_to_f16_rows, dim3((unsigned)B), dim3(256), 0, s, g.a, g.a_scale, a16,
                      rowscale, K);
   if (wide) {
@@ -773,8 +819,8 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
                          rowscale, g.w, g.w_sf, g.w_g, y, B, N, K, wtm, wtn);
   } else {
     const int tiles_m = (B + kTM - 1) / kTM, tiles_n = (N + kTN - 1) / kTN;
-    hipLaunchKernelGGL(gemm_tiled, dim3((unsigned)(tiles_m * tiles_n)), dim3(kTThreads), kTiledLds,
-                       s, a16, rowscale, g.w, g.w_sf, g.w_g, y, B, N, K, tiles_n);
+    hipLaunchKernelGGL(w_rows16 ? gemm_tiled<false> : gemm_tiled<true>, dim3((unsigned)(tiles_m * tiles_n)),
+                       dim3(kTThreads), kTiledLds, s, a16, rowscale, g.w, g.w_sf, g.w_g, y, B, N, K, tiles_n);
   }
   return hipGetLastError();
 }

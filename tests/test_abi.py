@@ -63,13 +63,21 @@ def test_quantize_validation_without_gpu(nv):
 def test_gemm_validation_without_gpu(nv):
     L = nv.lib()
     p = ctypes.c_void_p(256)
-    assert L.nvfp4_gemm(p, p, p, p, p, p, 4, 8, 48, None, 0, None) == nv.NVFP4_EINVAL   # K % 32
+    assert L.nvfp4_gemm(p, p, p, p, p, p, 4, 8, 40, None, 0, None) == nv.NVFP4_EINVAL   # K % 16
     assert L.nvfp4_gemm(None, p, p, p, p, p, 4, 8, 64, None, 0, None) == nv.NVFP4_EINVAL
-    assert L.nvfp4_gemm(p, p, ctypes.c_void_p(264), p, p, p, 4, 8, 64, None, 0, None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_gemm(p, ctypes.c_void_p(258), p, p, p, p, 4, 8, 64, None, 0, None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_gemm(p, p, p, p, p, ctypes.c_void_p(257), 4, 8, 64, None, 0, None) == nv.NVFP4_EINVAL
     assert L.nvfp4_gemm(p, p, p, p, p, p, 0, 8, 64, None, 0, None) == nv.NVFP4_OK
-    # large batches need a workspace
-    assert nv.gemm_workspace_size(4096, 8192, 8192) > 0
+    # large batches need a workspace, 256-byte aligned
+    need = nv.gemm_workspace_size(4096, 8192, 8192)
+    assert need > 0
     assert L.nvfp4_gemm(p, p, p, p, p, p, 4096, 8192, 8192, None, 0, None) == nv.NVFP4_EWORKSPACE
+    assert L.nvfp4_gemm(p, p, p, p, p, p, 4096, 8192, 8192, ctypes.c_void_p(4096 + 16), need,
+                        None) == nv.NVFP4_EWORKSPACE
+    assert L.nvfp4_gemm(p, p, p, p, p, p, 4096, 8192, 8192, ctypes.c_void_p(4096), need - 1,
+                        None) == nv.NVFP4_EWORKSPACE
+    assert L.nvfp4_gemm_pretiled(p, p, p, p, p, p, 4096, 8192, 8192, ctypes.c_void_p(4096 + 16), need,
+                                 None) == nv.NVFP4_EWORKSPACE
 
 
 def test_moe_validation_without_gpu(nv):
@@ -97,9 +105,11 @@ def test_external_weight_registry_without_gpu(nv):
     assert L.nvfp4_register_weight(1, 7, w, s, 64, 128, 8) == nv.NVFP4_OK          # other device
     assert L.nvfp4_register_weight(0, -1, w, s, 64, 128, 8) == nv.NVFP4_EINVAL     # baked-weight id
     assert L.nvfp4_register_weight(0, 8, w, s, 64, 128, 4) == nv.NVFP4_EINVAL      # scale_cols != K/16
-    assert L.nvfp4_register_weight(0, 8, w, s, 64, 48, 3) == nv.NVFP4_EINVAL       # K % 32 != 0
-    assert L.nvfp4_register_weight(0, 8, ctypes.c_void_p(4104), s, 64, 128, 8) == nv.NVFP4_EINVAL
+    assert L.nvfp4_register_weight(0, 8, w, s, 64, 40, 2) == nv.NVFP4_EINVAL       # K % 16 != 0
     assert L.nvfp4_register_weight(0, 8, None, s, 64, 128, 8) == nv.NVFP4_EINVAL
+    # K % 32 == 16 and unaligned pointers are accepted (the GEMM's byte-load path)
+    assert L.nvfp4_register_weight(0, 9, ctypes.c_void_p(4104), ctypes.c_void_p(8193), 64, 48, 3) == nv.NVFP4_OK
+    assert L.nvfp4_unregister_weight(0, 9) == nv.NVFP4_OK
     assert L.nvfp4_unregister_weight(0, 7) == nv.NVFP4_OK
     assert L.nvfp4_unregister_weight(0, 7) == nv.NVFP4_EINVAL
     assert L.nvfp4_unregister_weight(1, 7) == nv.NVFP4_OK
