@@ -99,6 +99,25 @@ def _check_dev(*ts):
             raise ValueError("tensors must be contiguous and on the GPU")
 
 
+def _need(t, name: str, dtype, shape=None, min_numel=None):
+    """Checks what the C ABI cannot: the dtype and the shape (or, for flat
+    buffers, the element count) of an operand or a caller-supplied output.  A
+    wrong one would be an out-of-bounds device access, so it is an error here."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError("%s must hold at least %d elements, got %d" % (name, min_numel, t.numel()))
+
+
+def _need_2d(x, name: str):
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("%s must be a 2-D tensor" % name)
+
+
 def _dtype_code(x: torch.Tensor) -> int:
     if x.dtype == torch.bfloat16:
         return NVFP4_BF16
@@ -111,10 +130,21 @@ def _workspace(nbytes: int, device, workspace: torch.Tensor | None):
     if nbytes == 0:
         return None, 0
     if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor")
         if workspace.numel() * workspace.element_size() < nbytes:
             raise ValueError("workspace too small: need %d bytes" % nbytes)
         return workspace, workspace.numel() * workspace.element_size()
     return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def _quant_out(o: dict, rows: int, k: int, ngroups: int):
+    """Checks a caller-supplied output dict of quantize() / act_quant()."""
+    _need(o.get("codes"), "out['codes']", torch.uint8, (rows, k // 2))
+    _need(o.get("sf"), "out['sf']", torch.uint8, (rows, k // 16))
+    _need(o.get("g_dec"), "out['g_dec']", torch.float32, min_numel=ngroups)
+    if o.get("scale") is not None:
+        _need(o["scale"], "out['scale']", torch.float32, (rows, k // 16))
 
 
 def quantize_workspace_size(rows: int, k: int, group_rows: int) -> int:
@@ -126,8 +156,12 @@ def quantize_workspace_size(rows: int, k: int, group_rows: int) -> int:
 def quantize(x: torch.Tensor, group_rows: int = 1, want_scale: bool = True, out: dict | None = None,
              workspace: torch.Tensor | None = None, stream=None) -> dict:
     """NVFP4-quantize x [rows, k] with one global scale per `group_rows` rows."""
-    _check_dev(x)
+    _need_2d(x, "x")
+    _dtype_code(x)
     rows, k = x.shape
+    if out is not None:
+        _quant_out(out, rows, k, rows // max(group_rows, 1))
+    _check_dev(x)
     dev = x.device
     o = out or {
         "codes": torch.empty((rows, k // 2), dtype=torch.uint8, device=dev),
@@ -146,10 +180,14 @@ def quantize(x: torch.Tensor, group_rows: int = 1, want_scale: bool = True, out:
 def act_quant(x: torch.Tensor, act: str = "none", want_scale: bool = True, out: dict | None = None,
               stream=None) -> dict:
     """Fused activation (none / swiglu / relu2) + per-token NVFP4 quantization."""
-    _check_dev(x)
+    _need_2d(x, "x")
+    _dtype_code(x)
     rows, k_in = x.shape
     a = ACT[act] if isinstance(act, str) else int(act)
     k_out = k_in // 2 if a == ACT["swiglu"] else k_in
+    if out is not None:
+        _quant_out(out, rows, k_out, rows)
+    _check_dev(x)
     dev = x.device
     o = out or {
         "codes": torch.empty((rows, k_out // 2), dtype=torch.uint8, device=dev),
@@ -172,13 +210,18 @@ def gemm(a_codes: torch.Tensor, a_scale: torch.Tensor, w_codes: torch.Tensor, w_
          w_g: torch.Tensor, out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
          stream=None) -> torch.Tensor:
     """y[B, N] fp16 = deq(a) . deq(w)^T."""
-    _check_dev(a_codes, a_scale, w_codes, w_sf, w_g)
+    _need_2d(a_codes, "a_codes")
+    _need_2d(w_codes, "w_codes")
     B, K = a_codes.shape[0], a_codes.shape[1] * 2
     N = w_codes.shape[0]
-    if w_codes.shape[1] * 2 != K or a_scale.shape != (B, K // 16) or w_sf.shape != (N, K // 16):
-        raise ValueError("operand shapes do not match the plugin contract")
-    if a_scale.dtype != torch.float32 or w_g.dtype != torch.float32 or w_g.numel() < 1:
-        raise TypeError("a_scale and w_g must be float32 (w_g holds one value)")
+    _need(a_codes, "a_codes", torch.uint8)
+    _need(a_scale, "a_scale", torch.float32, (B, K // 16))
+    _need(w_codes, "w_codes", torch.uint8, (N, K // 2))
+    _need(w_sf, "w_sf", torch.uint8, (N, K // 16))
+    _need(w_g, "w_g", torch.float32, min_numel=1)
+    if out is not None:
+        _need(out, "out", torch.float16, (B, N))
+    _check_dev(a_codes, a_scale, w_codes, w_sf, w_g, out)
     y = out if out is not None else torch.empty((B, N), dtype=torch.float16, device=a_codes.device)
     ws, wsb = _workspace(gemm_workspace_size(B, N, K), a_codes.device, workspace)
     st = _lib.nvfp4_gemm(_ptr(a_codes), _ptr(a_scale), _ptr(w_codes), _ptr(w_sf), _ptr(w_g), _ptr(y),
@@ -191,10 +234,11 @@ def gemm(a_codes: torch.Tensor, a_scale: torch.Tensor, w_codes: torch.Tensor, w_
 def pretile_weight(w_codes: torch.Tensor, w_sf: torch.Tensor, stream=None) -> dict:
     """The pre-tiled layout of [N, K/2] codes and [N, K/16] E4M3 bytes (flat
     uint8 tensors of N*K/2 and N*K/16 bytes)."""
-    _check_dev(w_codes, w_sf)
+    _need_2d(w_codes, "w_codes")
     N, K = w_codes.shape[0], w_codes.shape[1] * 2
-    if w_sf.shape != (N, K // 16) or w_codes.dtype != torch.uint8 or w_sf.dtype != torch.uint8:
-        raise ValueError("weight shapes do not match the plugin contract")
+    _need(w_codes, "w_codes", torch.uint8)
+    _need(w_sf, "w_sf", torch.uint8, (N, K // 16))
+    _check_dev(w_codes, w_sf)
     wt = torch.empty(N * K // 2, dtype=torch.uint8, device=w_codes.device)
     st = torch.empty(N * K // 16, dtype=torch.uint8, device=w_codes.device)
     rc = _lib.nvfp4_pretile_weight(_ptr(w_codes), _ptr(w_sf), N, K, _ptr(wt), _ptr(st), _stream(stream))
@@ -207,11 +251,19 @@ def gemm_pretiled(a_codes: torch.Tensor, a_scale: torch.Tensor, wt: dict, w_g: t
                   out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                   stream=None) -> torch.Tensor:
     """gemm() with weights from pretile_weight()."""
-    _check_dev(a_codes, a_scale, w_g, wt["codes"], wt["sf"])
+    _need_2d(a_codes, "a_codes")
     B, K = a_codes.shape[0], a_codes.shape[1] * 2
     N = wt["N"]
-    if K != wt["K"] or a_scale.shape != (B, K // 16) or a_scale.dtype != torch.float32:
-        raise ValueError("operand shapes do not match the plugin contract")
+    if K != wt["K"]:
+        raise ValueError("activation K %d differs from the pre-tiled weight's K %d" % (K, wt["K"]))
+    _need(a_codes, "a_codes", torch.uint8)
+    _need(a_scale, "a_scale", torch.float32, (B, K // 16))
+    _need(wt["codes"], "wt['codes']", torch.uint8, min_numel=N * K // 2)
+    _need(wt["sf"], "wt['sf']", torch.uint8, min_numel=N * K // 16)
+    _need(w_g, "w_g", torch.float32, min_numel=1)
+    if out is not None:
+        _need(out, "out", torch.float16, (B, N))
+    _check_dev(a_codes, a_scale, w_g, wt["codes"], wt["sf"], out)
     y = out if out is not None else torch.empty((B, N), dtype=torch.float16, device=a_codes.device)
     ws, wsb = _workspace(gemm_workspace_size(B, N, K), a_codes.device, workspace)
     rc = _lib.nvfp4_gemm_pretiled(_ptr(a_codes), _ptr(a_scale), _ptr(wt["codes"]), _ptr(wt["sf"]), _ptr(w_g),
@@ -225,10 +277,11 @@ def register_weight(resource_id: int, w_codes: torch.Tensor, w_sf: torch.Tensor)
     """Registers an external weight ([N, K/2] codes, [N, K/16] E4M3 bytes) for
     (the tensors' device, resource_id).  The tensors must outlive the
     registration: unregister before freeing them."""
-    _check_dev(w_codes, w_sf)
+    _need_2d(w_codes, "w_codes")
     N, K = w_codes.shape[0], w_codes.shape[1] * 2
-    if w_sf.shape != (N, K // 16) or w_codes.dtype != torch.uint8 or w_sf.dtype != torch.uint8:
-        raise ValueError("weight shapes do not match the plugin contract")
+    _need(w_codes, "w_codes", torch.uint8)
+    _need(w_sf, "w_sf", torch.uint8, (N, K // 16))
+    _check_dev(w_codes, w_sf)
     st = _lib.nvfp4_register_weight(w_codes.device.index or 0, resource_id, _ptr(w_codes), _ptr(w_sf),
                                     N, K, K // 16)
     if st != NVFP4_OK:
@@ -245,10 +298,14 @@ def gemm_external(a_codes: torch.Tensor, a_scale: torch.Tensor, resource_id: int
                   w_g: torch.Tensor, out: torch.Tensor | None = None,
                   workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """gemm() with the weight registered under resource_id on the current device."""
-    _check_dev(a_codes, a_scale, w_g)
+    _need_2d(a_codes, "a_codes")
     B, K = a_codes.shape[0], a_codes.shape[1] * 2
-    if a_scale.shape != (B, K // 16) or a_scale.dtype != torch.float32 or w_g.dtype != torch.float32:
-        raise ValueError("activation operands do not match the plugin contract")
+    _need(a_codes, "a_codes", torch.uint8)
+    _need(a_scale, "a_scale", torch.float32, (B, K // 16))
+    _need(w_g, "w_g", torch.float32, min_numel=1)
+    if out is not None:
+        _need(out, "out", torch.float16, (B, N))
+    _check_dev(a_codes, a_scale, w_g, out)
     y = out if out is not None else torch.empty((B, N), dtype=torch.float16, device=a_codes.device)
     ws, wsb = _workspace(gemm_workspace_size(B, N, K), a_codes.device, workspace)
     st = _lib.nvfp4_gemm_external(_ptr(a_codes), _ptr(a_scale), resource_id, _ptr(w_g), _ptr(y),
@@ -266,12 +323,25 @@ def moe_w4a16(logits, bias, x, w1, w1_sf, w1_g, w2, w2_sf, w2_g, top_k, n_group,
               norm_topk_prob=True, routed_scaling=1.0, out=None, want_routing=False,
               workspace=None, stream=None):
     """Routed W4A16 MoE layer; returns out (and (ids, weights) if want_routing)."""
-    _check_dev(logits, bias, x, w1, w1_sf, w1_g, w2, w2_sf, w2_g)
+    _need_2d(logits, "logits")
+    _need_2d(x, "x")
     T, E = logits.shape
     hidden = x.shape[1]
+    if not isinstance(w1, torch.Tensor) or w1.dim() != 3:
+        raise ValueError("w1 must be a 3-D tensor [experts, inter, hidden/2]")
     inter = w1.shape[1]
-    if x.dtype != torch.float16:
-        raise TypeError("hidden states must be float16")
+    _need(logits, "logits", torch.float32)
+    _need(bias, "bias", torch.float32, (E,))
+    _need(x, "x", torch.float16, (T, hidden))
+    _need(w1, "w1", torch.uint8, (E, inter, hidden // 2))
+    _need(w1_sf, "w1_sf", torch.uint8, (E, inter, hidden // 16))
+    _need(w1_g, "w1_g", torch.float32, min_numel=E)
+    _need(w2, "w2", torch.uint8, (E, hidden, inter // 2))
+    _need(w2_sf, "w2_sf", torch.uint8, (E, hidden, inter // 16))
+    _need(w2_g, "w2_g", torch.float32, min_numel=E)
+    if out is not None:
+        _need(out, "out", torch.float16, (T, hidden))
+    _check_dev(logits, bias, x, w1, w1_sf, w1_g, w2, w2_sf, w2_g, out)
     o = out if out is not None else torch.empty((T, hidden), dtype=torch.float16, device=x.device)
     ids = torch.empty((T, top_k), dtype=torch.int32, device=x.device) if want_routing else None
     wts = torch.empty((T, top_k), dtype=torch.float32, device=x.device) if want_routing else None
@@ -299,10 +369,21 @@ def mx_quantize(x: torch.Tensor, act: str = "none", group_rows: int = 1, tiled: 
     optional activation in front.  Returns dict(codes, sf, g_dec, rows, K, tiled):
     [rows, k/2] and [rows, k/32] uint8 in the row layout, flat uint8 tensors in
     the MX tile layout."""
-    _check_dev(x)
+    _need_2d(x, "x")
+    _dtype_code(x)
     rows, k_in = x.shape
     a = ACT[act] if isinstance(act, str) else int(act)
     k = k_in // 2 if a == ACT["swiglu"] else k_in
+    if out is not None:
+        if tiled:
+            nc, ns = mx_tiled_sizes(rows, k)
+            _need(out.get("codes"), "out['codes']", torch.uint8, min_numel=nc)
+            _need(out.get("sf"), "out['sf']", torch.uint8, min_numel=ns)
+        else:
+            _need(out.get("codes"), "out['codes']", torch.uint8, (rows, k // 2))
+            _need(out.get("sf"), "out['sf']", torch.uint8, (rows, k // 32))
+        _need(out.get("g_dec"), "out['g_dec']", torch.float32, min_numel=rows // max(group_rows, 1))
+    _check_dev(x)
     dev = x.device
     if out is None:
         if tiled:
@@ -326,10 +407,11 @@ def mx_quantize(x: torch.Tensor, act: str = "none", group_rows: int = 1, tiled: 
 
 def mx_tile(codes: torch.Tensor, sf: torch.Tensor, stream=None) -> dict:
     """The MX tile layout of [rows, k/2] codes and [rows, k/32] E8M0 bytes."""
-    _check_dev(codes, sf)
+    _need_2d(codes, "codes")
     rows, k = codes.shape[0], codes.shape[1] * 2
-    if sf.shape != (rows, k // 32) or codes.dtype != torch.uint8 or sf.dtype != torch.uint8:
-        raise ValueError("codes [rows, k/2] and E8M0 bytes [rows, k/32] expected")
+    _need(codes, "codes", torch.uint8)
+    _need(sf, "sf", torch.uint8, (rows, k // 32))
+    _check_dev(codes, sf)
     nc, ns = mx_tiled_sizes(rows, k)
     ct = torch.empty(nc, dtype=torch.uint8, device=codes.device)
     stt = torch.empty(ns, dtype=torch.uint8, device=codes.device)
@@ -345,7 +427,6 @@ def mx_gemm(a: dict, a_g: torch.Tensor, w: dict, w_g: torch.Tensor, a_group_rows
     (dicts from mx_quantize(tiled=True) or mx_tile)."""
     if not (a.get("tiled") and w.get("tiled")):
         raise ValueError("mx_gemm takes operands in the MX tile layout")
-    _check_dev(a["codes"], a["sf"], a_g, w["codes"], w["sf"], w_g)
     B, N, K = a["rows"], w["rows"], a["K"]
     if w["K"] != K:
         raise ValueError("operand K differs")
@@ -354,8 +435,11 @@ def mx_gemm(a: dict, a_g: torch.Tensor, w: dict, w_g: torch.Tensor, a_group_rows
         if op["codes"].dtype != torch.uint8 or op["sf"].dtype != torch.uint8 or \
                 op["codes"].numel() < nc or op["sf"].numel() < ns:
             raise ValueError("tile buffers smaller than the MX tile layout of %d x %d" % (r, K))
-    if a_g.dtype != torch.float32 or w_g.dtype != torch.float32:
-        raise TypeError("globals must be float32")
+    _need(a_g, "a_g", torch.float32, min_numel=B // max(a_group_rows, 1))
+    _need(w_g, "w_g", torch.float32, min_numel=1)
+    if out is not None:
+        _need(out, "out", torch.float16, (B, N))
+    _check_dev(a["codes"], a["sf"], a_g, w["codes"], w["sf"], w_g, out)
     y = out if out is not None else torch.empty((B, N), dtype=torch.float16, device=a["codes"].device)
     rc = _lib.nvfp4_mx_gemm(_ptr(a["codes"]), _ptr(a["sf"]), _ptr(a_g), a_group_rows, _ptr(w["codes"]),
                             _ptr(w["sf"]), _ptr(w_g), _ptr(y), B, N, K, _stream(stream))
