@@ -59,6 +59,7 @@ extern "C" {
 #define NVFP4_EUNSUPPORTED 2  /* current device is not gfx950, or size beyond limits */
 #define NVFP4_EWORKSPACE 3    /* workspace missing or smaller than the query returns */
 #define NVFP4_EHIP 4          /* a HIP runtime call or launch failed */
+#define NVFP4_ESCRATCH 5      /* needs more than the fixed scratch of a no-allocation entry point */
 
 /* Input element types. */
 #define NVFP4_BF16 0
@@ -239,6 +240,33 @@ int32_t nvfp4_moe_w4a16(const float* router_logits, const float* correction_bias
                         float routed_scaling, void* workspace, size_t workspace_bytes, void* stream);
 size_t nvfp4_moe_w4a16_workspace_size(int32_t tokens, int32_t experts, int32_t top_k, int32_t hidden,
                                       int32_t inter);
+
+/*
+ * nvfp4_moe_w4a16_noalloc -- nvfp4_moe_w4a16 for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments without the workspace, the same
+ * kernels and the same results (bit-identical).  Its scratch is a fixed
+ * device array of NVFP4_NOALLOC_SCRATCH_BYTES inside the library; each GPU the
+ * library runs on holds its own copy from the first call until the process
+ * ends.  The call allocates and frees nothing.
+ *   Returns NVFP4_ESCRATCH (nothing launched) when
+ *   nvfp4_moe_w4a16_workspace_size(tokens, experts, top_k, hidden, inter)
+ *   exceeds NVFP4_NOALLOC_SCRATCH_BYTES (32 MiB: e.g. up to ~400 tokens at
+ *   64 experts, top-8, hidden 2048, inter 1024); otherwise as nvfp4_moe_w4a16.
+ * Every call on one GPU uses that GPU's one array: calls that overlap in time
+ * on one GPU (concurrent streams, or host threads without ordering between
+ * their streams) race and give undefined results.  No part of the scratch
+ * needs to start at zero: every word a call reads was written earlier in the
+ * same call, so contents left by the previous call do not matter.
+ */
+#define NVFP4_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+int32_t nvfp4_moe_w4a16_noalloc(const float* router_logits, const float* correction_bias,
+                                const void* x, const uint8_t* w1, const uint8_t* w1_sf,
+                                const float* w1_g, const uint8_t* w2, const uint8_t* w2_sf,
+                                const float* w2_g, void* out, int32_t* topk_ids_out,
+                                float* topk_w_out, int32_t tokens, int32_t experts, int32_t top_k,
+                                int32_t hidden, int32_t inter, int32_t n_group, int32_t topk_group,
+                                int32_t norm_topk_prob, float routed_scaling, void* stream);
 
 /*
  * MXFP4 variant -- the UE8M0_SF switch of the block helper in "perf: optimize

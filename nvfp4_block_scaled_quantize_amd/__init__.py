@@ -15,7 +15,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnvfp4_mi355x.so")
 
-NVFP4_OK, NVFP4_EINVAL, NVFP4_EUNSUPPORTED, NVFP4_EWORKSPACE, NVFP4_EHIP = range(5)
+NVFP4_OK, NVFP4_EINVAL, NVFP4_EUNSUPPORTED, NVFP4_EWORKSPACE, NVFP4_EHIP, NVFP4_ESCRATCH = range(6)
+NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024   # NVFP4_NOALLOC_SCRATCH_BYTES
 NVFP4_BF16, NVFP4_FP16 = 0, 1
 ACT = {"none": 0, "swiglu": 1, "relu2": 2}
 
@@ -24,7 +25,7 @@ EXPORTS = [
     "nvfp4_gemm", "nvfp4_gemm_workspace_size", "nvfp4_moe_w4a16", "nvfp4_moe_w4a16_workspace_size",
     "nvfp4_register_weight", "nvfp4_unregister_weight", "nvfp4_gemm_external",
     "nvfp4_pretile_weight", "nvfp4_gemm_pretiled", "nvfp4_mx_quantize", "nvfp4_mx_tile",
-    "nvfp4_mx_gemm",
+    "nvfp4_mx_gemm", "nvfp4_moe_w4a16_noalloc",
 ]
 MX_ROWS, MX_TILED = 0, 1
 
@@ -56,6 +57,9 @@ def _load() -> ctypes.CDLL:
     L.nvfp4_moe_w4a16.argtypes = [p, p, p, p, p, p, p, p, p, p, p, p,
                                   i32, i32, i32, i32, i32, i32, i32, i32, f32, p, sz, p]
     L.nvfp4_moe_w4a16.restype = i32
+    L.nvfp4_moe_w4a16_noalloc.argtypes = [p, p, p, p, p, p, p, p, p, p, p, p,
+                                          i32, i32, i32, i32, i32, i32, i32, i32, f32, p]
+    L.nvfp4_moe_w4a16_noalloc.restype = i32
     L.nvfp4_moe_w4a16_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     L.nvfp4_moe_w4a16_workspace_size.restype = sz
     L.nvfp4_register_weight.argtypes = [i32, i32, p, p, i32, i32, i32]
@@ -353,6 +357,41 @@ def moe_w4a16(logits, bias, x, w1, w1_sf, w1_g, w2, w2_sf, w2_g, top_k, n_group,
     if st != NVFP4_OK:
         raise Nvfp4Error(st, "nvfp4_moe_w4a16")
     return (o, ids, wts) if want_routing else o
+
+
+def moe_w4a16_noalloc(logits, bias, x, w1, w1_sf, w1_g, w2, w2_sf, w2_g, top_k, n_group, topk_group,
+                      norm_topk_prob=True, routed_scaling=1.0, out=None, ids_out=None, w_out=None, stream=None):
+    """moe_w4a16() on the library's fixed device scratch: no workspace, nothing
+    allocated by the library (pass `out` to allocate nothing here either).
+    Calls that overlap in time on one GPU race."""
+    _need_2d(logits, "logits")
+    _need_2d(x, "x")
+    T, E = logits.shape
+    hidden = x.shape[1]
+    if not isinstance(w1, torch.Tensor) or w1.dim() != 3:
+        raise ValueError("w1 must be a 3-D tensor [experts, inter, hidden/2]")
+    inter = w1.shape[1]
+    _need(logits, "logits", torch.float32)
+    _need(bias, "bias", torch.float32, (E,))
+    _need(x, "x", torch.float16, (T, hidden))
+    _need(w1, "w1", torch.uint8, (E, inter, hidden // 2))
+    _need(w1_sf, "w1_sf", torch.uint8, (E, inter, hidden // 16))
+    _need(w1_g, "w1_g", torch.float32, min_numel=E)
+    _need(w2, "w2", torch.uint8, (E, hidden, inter // 2))
+    _need(w2_sf, "w2_sf", torch.uint8, (E, hidden, inter // 16))
+    _need(w2_g, "w2_g", torch.float32, min_numel=E)
+    for t, name, dt in ((out, "out", torch.float16), (ids_out, "ids_out", torch.int32), (w_out, "w_out", torch.float32)):
+        if t is not None:
+            _need(t, name, dt, (T, hidden) if name == "out" else (T, top_k))
+    _check_dev(logits, bias, x, w1, w1_sf, w1_g, w2, w2_sf, w2_g, out, ids_out, w_out)
+    o = out if out is not None else torch.empty((T, hidden), dtype=torch.float16, device=x.device)
+    st = _lib.nvfp4_moe_w4a16_noalloc(_ptr(logits), _ptr(bias), _ptr(x), _ptr(w1), _ptr(w1_sf), _ptr(w1_g),
+                                      _ptr(w2), _ptr(w2_sf), _ptr(w2_g), _ptr(o), _ptr(ids_out), _ptr(w_out),
+                                      T, E, top_k, hidden, inter, n_group, topk_group, int(bool(norm_topk_prob)),
+                                      float(routed_scaling), _stream(stream))
+    if st != NVFP4_OK:
+        raise Nvfp4Error(st, "nvfp4_moe_w4a16_noalloc")
+    return o
 
 
 # ---------------------------------------------------------------- MXFP4 variant

@@ -78,6 +78,7 @@ const char* nvfp4_status_string(int32_t status) {
     case NVFP4_EUNSUPPORTED: return "unsupported device or size";
     case NVFP4_EWORKSPACE: return "workspace missing or too small";
     case NVFP4_EHIP: return "HIP runtime error";
+    case NVFP4_ESCRATCH: return "problem larger than the fixed scratch of the no-allocation entry point";
     default: return "unknown status";
   }
 }
@@ -300,13 +301,13 @@ size_t nvfp4_moe_w4a16_workspace_size(int32_t tokens, int32_t experts, int32_t t
   return nvfp4::moe_workspace_bytes(tokens, experts, top_k, hidden, inter);
 }
 
-int32_t nvfp4_moe_w4a16(const float* router_logits, const float* correction_bias, const void* x,
-                        const uint8_t* w1, const uint8_t* w1_sf, const float* w1_g,
-                        const uint8_t* w2, const uint8_t* w2_sf, const float* w2_g, void* out,
-                        int32_t* topk_ids_out, float* topk_w_out, int32_t tokens, int32_t experts,
-                        int32_t top_k, int32_t hidden, int32_t inter, int32_t n_group,
-                        int32_t topk_group, int32_t norm_topk_prob, float routed_scaling,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+// Argument checks shared by both MoE entry points (everything but the
+// workspace); NVFP4_OK for tokens == 0 too (the caller returns early).
+static int32_t moe_check(const float* router_logits, const float* correction_bias, const void* x,
+                         const uint8_t* w1, const uint8_t* w1_sf, const float* w1_g,
+                         const uint8_t* w2, const uint8_t* w2_sf, const float* w2_g, void* out,
+                         int32_t tokens, int32_t experts, int32_t top_k, int32_t hidden,
+                         int32_t inter, int32_t n_group, int32_t topk_group) {
   if (tokens < 0 || tokens > (1 << 24) || experts <= 0 || experts > 256 || n_group <= 0 ||
       experts % n_group != 0)
     return NVFP4_EINVAL;
@@ -324,6 +325,19 @@ int32_t nvfp4_moe_w4a16(const float* router_logits, const float* correction_bias
       ((uintptr_t)w2 % 16) != 0 || ((uintptr_t)w1_sf % 2) != 0 || ((uintptr_t)w2_sf % 2) != 0 ||
       !aligned4(router_logits) || !aligned4(correction_bias) || !aligned4(w1_g) || !aligned4(w2_g))
     return NVFP4_EINVAL;
+  return NVFP4_OK;
+}
+
+int32_t nvfp4_moe_w4a16(const float* router_logits, const float* correction_bias, const void* x,
+                        const uint8_t* w1, const uint8_t* w1_sf, const float* w1_g,
+                        const uint8_t* w2, const uint8_t* w2_sf, const float* w2_g, void* out,
+                        int32_t* topk_ids_out, float* topk_w_out, int32_t tokens, int32_t experts,
+                        int32_t top_k, int32_t hidden, int32_t inter, int32_t n_group,
+                        int32_t topk_group, int32_t norm_topk_prob, float routed_scaling,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  const int32_t st = moe_check(router_logits, correction_bias, x, w1, w1_sf, w1_g, w2, w2_sf, w2_g,
+                               out, tokens, experts, top_k, hidden, inter, n_group, topk_group);
+  if (st != NVFP4_OK || tokens == 0) return st;
   const size_t need = nvfp4::moe_workspace_bytes(tokens, experts, top_k, hidden, inter);
   if (!workspace || workspace_bytes < need || !aligned256(workspace)) return NVFP4_EWORKSPACE;
   const int32_t ds = device_status();
@@ -331,6 +345,31 @@ int32_t nvfp4_moe_w4a16(const float* router_logits, const float* correction_bias
   nvfp4::MoeArgs m{router_logits, correction_bias, x, w1, w1_sf, w1_g, w2, w2_sf, w2_g, out,
                    topk_ids_out, topk_w_out, tokens, experts, top_k, hidden, inter, n_group,
                    topk_group, norm_topk_prob ? 1 : 0, routed_scaling, workspace, workspace_bytes,
+                   current_device()->num_cus};
+  return hip_status(nvfp4::launch_moe(m, (hipStream_t)stream));
+}
+
+int32_t nvfp4_moe_w4a16_noalloc(const float* router_logits, const float* correction_bias,
+                                const void* x, const uint8_t* w1, const uint8_t* w1_sf,
+                                const float* w1_g, const uint8_t* w2, const uint8_t* w2_sf,
+                                const float* w2_g, void* out, int32_t* topk_ids_out,
+                                float* topk_w_out, int32_t tokens, int32_t experts, int32_t top_k,
+                                int32_t hidden, int32_t inter, int32_t n_group, int32_t topk_group,
+                                int32_t norm_topk_prob, float routed_scaling, void* stream) {
+  const int32_t st = moe_check(router_logits, correction_bias, x, w1, w1_sf, w1_g, w2, w2_sf, w2_g,
+                               out, tokens, experts, top_k, hidden, inter, n_group, topk_group);
+  if (st != NVFP4_OK || tokens == 0) return st;
+  const size_t need = nvfp4::moe_workspace_bytes(tokens, experts, top_k, hidden, inter);
+  if (need > (size_t)NVFP4_NOALLOC_SCRATCH_BYTES) return NVFP4_ESCRATCH;
+  const int32_t ds = device_status();
+  if (ds != NVFP4_OK) return ds;
+  void* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  if (nvfp4::moe_noalloc_scratch(&scratch, &scratch_bytes) != hipSuccess || scratch_bytes < need)
+    return NVFP4_EHIP;
+  nvfp4::MoeArgs m{router_logits, correction_bias, x, w1, w1_sf, w1_g, w2, w2_sf, w2_g, out,
+                   topk_ids_out, topk_w_out, tokens, experts, top_k, hidden, inter, n_group,
+                   topk_group, norm_topk_prob ? 1 : 0, routed_scaling, scratch, scratch_bytes,
                    current_device()->num_cus};
   return hip_status(nvfp4::launch_moe(m, (hipStream_t)stream));
 }

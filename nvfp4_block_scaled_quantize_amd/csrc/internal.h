@@ -91,5 +91,7 @@ hipError_t launch_mx_gemm(const MxGemmArgs& g, hipStream_t s);
 
 size_t moe_workspace_bytes(int tokens, int experts, int top_k, int hidden, int inter);
 hipError_t launch_moe(const MoeArgs& m, hipStream_t s);
+// The fixed no-allocation scratch of the current device (address and size).
+hipError_t moe_noalloc_scratch(void** ptr, size_t* bytes);
 
 }  // namespace nvfp4

@@ -31,6 +31,16 @@
 //  5. combine    : out[t] = sum_j w[t,j] * o[t*top_k + j] in rank order, FP16.
 #include "device_common.h"
 #include "internal.h"
+#include "../../include/nvfp4_mi355x.h"
+
+#include <mutex>
+
+// Fixed device scratch of nvfp4_moe_w4a16_noalloc, for callers that cannot
+// allocate.  Each GPU the library runs on holds its own copy until the
+// process ends.  In host code `scratch` is only a host-side stand-in: the
+// device address comes from moe_noalloc_scratch() below and is what the
+// kernels receive.
+static __device__ __align__(256) unsigned char scratch[NVFP4_NOALLOC_SCRATCH_BYTES];
 
 namespace nvfp4 {
 
@@ -654,6 +664,28 @@ static int tiles_per_wg(int experts, int n, int num_cus) {
   const int units = experts * ((n + kFwRows - 1) / kFwRows);
   int r = num_cus > 0 ? units / num_cus : 1;
   return r < 1 ? 1 : (r > 8 ? 8 : r);
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+hipError_t moe_noalloc_scratch(void** ptr, size_t* bytes) {
+  constexpr int kMaxDev = 64;
+  static std::once_flag once[kMaxDev];
+  static void* addr[kMaxDev];
+  static hipError_t err[kMaxDev];
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [dev]() {
+    void* p = nullptr;
+    err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    addr[dev] = (err[dev] == hipSuccess) ? p : nullptr;
+  });
+  if (err[dev] != hipSuccess) return err[dev];
+  *ptr = addr[dev];
+  *bytes = sizeof(scratch);
+  return hipSuccess;
 }
 
 hipError_t launch_moe(const MoeArgs& m, hipStream_t s) {

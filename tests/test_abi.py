@@ -93,6 +93,15 @@ def test_moe_validation_without_gpu(nv):
     assert L.nvfp4_moe_w4a16(*args, 4, 8, 2, 64, 32, 4, 2, 1, 1.0, None, 0, None) == nv.NVFP4_EINVAL
     # missing workspace
     assert L.nvfp4_moe_w4a16(*args, 4, 8, 2, 64, 64, 4, 2, 1, 1.0, None, 0, None) == nv.NVFP4_EWORKSPACE
+    # the no-allocation variant: same argument checks; a problem whose
+    # workspace exceeds its fixed scratch is refused before any launch
+    assert L.nvfp4_moe_w4a16_noalloc(*args, 4, 10, 2, 64, 64, 3, 1, 1, 1.0, None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_moe_w4a16_noalloc(*args, 0, 8, 2, 64, 64, 4, 2, 1, 1.0, None) == nv.NVFP4_OK
+    big = (4096, 64, 8, 2048, 1024)
+    assert nv.moe_workspace_size(*big) > nv.NOALLOC_SCRATCH_BYTES
+    assert L.nvfp4_moe_w4a16_noalloc(*args, *big[:3], 2048, 1024, 8, 4, 1, 1.0, None) == nv.NVFP4_ESCRATCH
+    assert nv.moe_workspace_size(256, 64, 8, 2048, 1024) <= nv.NOALLOC_SCRATCH_BYTES   # the C5 layer fits
+    assert L.nvfp4_status_string(nv.NVFP4_ESCRATCH).startswith(b"problem larger")
 
 
 def test_external_weight_registry_without_gpu(nv):
