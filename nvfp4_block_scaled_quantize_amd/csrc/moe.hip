@@ -48,6 +48,23 @@ namespace {
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// Expert FFN kernels (moe_fc_wide below): work split and staging.
+constexpr int kFwThreads = 512;
+constexpr int kFwRows = 256;              // weight rows per tile (32 per wave)
+constexpr int kFwKC = 128;                // k per chunk
+constexpr int kFwTT = 2;                  // 32-token MFMA tiles per pass
+constexpr int kFwTok = 32 * kFwTT;        // tokens per pass at most
+constexpr int kFwPitch = kFwKC + 8;       // halves per staged token row (+16 B skew)
+constexpr int kFwVec = kFwTok * kFwKC / 8 / kFwThreads;   // staged 8-element vectors per thread
+constexpr int kFwRowThreads = kFwKC / 8;  // threads staging one token row of a chunk
+constexpr int kFwSlotsPerVec = kFwThreads / kFwRowThreads;   // token slots per staged vector index
+constexpr int kFwWBuf = 4;                // weight register buffers (loads three chunks ahead)
+constexpr int kFwMaxZ = 1024;             // grid z (more passes handled in a loop)
+constexpr int kFwMaxT1 = 8192 / kFwRows;  // fc1 row tiles (inter <= 8192)
+constexpr int kFwPerCU = 512 / kFwThreads;   // workgroups resident per compute unit
+static_assert(kFwVec * kFwSlotsPerVec == kFwTok, "staging covers the pass's token slots");
+static_assert(kFwRows == 32 * (kFwThreads / 64), "one 32-row MFMA tile per wave");
+
 struct MoeWs {
   int32_t* ids;      // [P] expert of each pair
   float* wts;        // [P] its weight
@@ -60,7 +77,7 @@ struct MoeWs {
   float* o;          // [P, hidden]
 };
 
-int fc1_tiles(int inter) { return (inter + 255) / 256; }
+int fc1_tiles(int inter) { return (inter + kFwRows - 1) / kFwRows; }
 
 MoeWs carve(void* base, int T, int E, int P, int hidden, int inter) {
   unsigned char* p = reinterpret_cast<unsigned char*>(base);
@@ -316,16 +333,6 @@ __device__ __forceinline__ v8h dequant8_w(uint32_t codes, _Float16 s16) {
 // FC = 2: act = h [P, K]; staging rescales each 256-k tile by 2^(et - e),
 //         e = exponent of pmax[p], so the pair's values share one scale and
 //         none can overflow FP16.  out = o [P, N] fp32 = h . W^T * g * 2^e.
-constexpr int kFwThreads = 512;
-constexpr int kFwRows = 256;              // weight rows per tile
-constexpr int kFwKC = 128;                // k per chunk
-constexpr int kFwTT = 2;                  // 32-token MFMA tiles per pass
-constexpr int kFwTok = 32 * kFwTT;        // tokens per pass at most
-constexpr int kFwPitch = kFwKC + 8;       // halves per staged token row (+16 B skew)
-constexpr int kFwVec = kFwTok * kFwKC / 8 / kFwThreads;   // staged 8-element vectors per thread
-constexpr int kFwWBuf = 4;                // weight register buffers (loads three chunks ahead)
-constexpr int kFwMaxZ = 1024;             // grid z (more passes handled in a loop)
-constexpr int kFwMaxT1 = 32;              // fc1 row tiles (inter <= 8192)
 
 // Workgroup barrier that waits only for this wave's LDS operations.
 // __syncthreads() also waits for every outstanding global load, which would
@@ -411,8 +418,8 @@ moe_fc_wide(const _Float16* __restrict__ act, const int32_t* __restrict__ plists
     d.sc = *reinterpret_cast<const uint32_t*>(sr + k / 16);
   };
 
-  // staging: vector i of a thread = token slot (tid + 512 i) / 16 = 32 i +
-  // tid / 16 (token tile i), 8 k at 8 (tid % 16); only the pass's token
+  // staging: vector i of a thread = token slot kFwSlotsPerVec * i + tid /
+  // kFwRowThreads, 8 k at 8 (tid % kFwRowThreads); only the pass's token
   // tiles are staged
   v8h stg[kFwWBuf][kFwVec];
   const int kq = tid % (kFwKC / 8);
@@ -431,19 +438,20 @@ moe_fc_wide(const _Float16* __restrict__ act, const int32_t* __restrict__ plists
   };
   auto stage_store = [&](int c, const v8h (&src)[kFwVec], _Float16* xb, int ntt) __attribute__((always_inline)) {
     const bool kv = c * kFwKC + 8 * kq < K;
-    const int t = (c >> 1) < nt1 ? (c >> 1) : nt1 - 1;   // fc2: fc1 row tile of the chunk
+    const int ct = c * kFwKC / kFwRows;   // fc2: fc1 row tile of the chunk
+    const int t = ct < nt1 ? ct : nt1 - 1;
 #pragma unroll
     for (int i = 0; i < kFwVec; ++i) {
-      if (i < ntt) {
+      if (kFwSlotsPerVec * i / 32 < ntt) {
         v8h val = src[i];
         if constexpr (FC == 2) {
-          const _Float16 f = sfac[t][32 * i + tid / 16];
+          const _Float16 f = sfac[t][kFwSlotsPerVec * i + tid / kFwRowThreads];
           const v2h f2 = {f, f};
           v2h* pv = reinterpret_cast<v2h*>(&val);
           pv[0] = pv[0] * f2; pv[1] = pv[1] * f2; pv[2] = pv[2] * f2; pv[3] = pv[3] * f2;
         }
         if (!(kv && sval[i])) val = v8h{0, 0, 0, 0, 0, 0, 0, 0};
-        *reinterpret_cast<v8h*>(xb + (32 * i + tid / 16) * kFwPitch + 8 * kq) = val;
+        *reinterpret_cast<v8h*>(xb + (kFwSlotsPerVec * i + tid / kFwRowThreads) * kFwPitch + 8 * kq) = val;
       }
     }
   };
@@ -578,7 +586,7 @@ moe_fc_wide(const _Float16* __restrict__ act, const int32_t* __restrict__ plists
     lds_barrier();
 #pragma unroll
     for (int i = 0; i < kFwVec; ++i) {
-      const int slot = 32 * i + tid / 16;
+      const int slot = kFwSlotsPerVec * i + tid / kFwRowThreads;
       sval[i] = slot < ntok;
       abase[i] = (int64_t)srow[slot] * K;
     }
@@ -662,7 +670,8 @@ size_t moe_workspace_bytes(int tokens, int experts, int top_k, int hidden, int i
 // layer split evenly over the compute units when there are more of them.
 static int tiles_per_wg(int experts, int n, int num_cus) {
   const int units = experts * ((n + kFwRows - 1) / kFwRows);
-  int r = num_cus > 0 ? units / num_cus : 1;
+  const int slots = num_cus * kFwPerCU;
+  int r = slots > 0 ? units / slots : 1;
   return r < 1 ? 1 : (r > 8 ? 8 : r);
 }
 
