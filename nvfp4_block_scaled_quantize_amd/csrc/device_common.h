@@ -163,6 +163,14 @@ __device__ __forceinline__ uint32_t pack8_e2m1(const float* v, float enc) {
   return w;
 }
 
+// ---------------------------------------------------------------- barriers
+// Workgroup barrier that waits only for this wave's LDS operations.
+// __syncthreads() also waits for every outstanding global load (vmcnt(0)),
+// which would drain the loads a streaming kernel keeps in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -334,12 +334,6 @@ __device__ __forceinline__ v8h dequant8_w(uint32_t codes, _Float16 s16) {
 //         e = exponent of pmax[p], so the pair's values share one scale and
 //         none can overflow FP16.  out = o [P, N] fp32 = h . W^T * g * 2^e.
 
-// Workgroup barrier that waits only for this wave's LDS operations.
-// __syncthreads() also waits for every outstanding global load, which would
-// drain the weight loads issued chunks ahead at every chunk.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 template <int V> struct IntC { static constexpr int value = V; };
 
