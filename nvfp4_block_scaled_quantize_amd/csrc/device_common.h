@@ -186,12 +186,17 @@ __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-// Max over the 64 lanes of a wave, returned as a wave-uniform value.
-__device__ __forceinline__ float wave_max_dpp(float v) {
+// Max over each row of 16 lanes; every lane of the row receives it.
+__device__ __forceinline__ float row16_max(float v) {
   v = __builtin_fmaxf(v, dpp_f32<0xB1>(v));
   v = __builtin_fmaxf(v, dpp_f32<0x4E>(v));
   v = __builtin_fmaxf(v, dpp_f32<0x141>(v));
-  v = __builtin_fmaxf(v, dpp_f32<0x140>(v));   // every lane of a 16-lane row holds the row max
+  return __builtin_fmaxf(v, dpp_f32<0x140>(v));
+}
+
+// Max over the 64 lanes of a wave, returned as a wave-uniform value.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = row16_max(v);
   const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
   const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
   const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));

@@ -7,27 +7,31 @@
 // and the activation side an arbitrary FP32 scale per 16 elements.  The
 // dequantized weight e2m1 * e4m3 has at most 6 significant bits and lies in
 // [2^-10, 2688], so it is EXACT in FP16; the global weight scale moves to the
-// epilogue.  The activation q * c is rounded once to FP16 after a per-row
-// power-of-two normalization (so no row can overflow FP16), and the row's
-// power of two returns in the epilogue.  Products accumulate in FP32.
+// epilogue.  The activation q * c is rounded once to FP16 after a power-of-two
+// normalization (per row for the prefill kernels, per row and half round of
+// 256 k in the decode kernel) so that no value can overflow FP16; the power of
+// two returns in FP32 after the MFMAs.  Products accumulate in FP32.
 //
-// Two kernels, chosen by the batch size:
+// Two kernel families, chosen by the batch size:
 //  * gemm_skinny (B <= 16, decode): a streaming GEMV-like pass over the weight
-//    matrix.  Each wave owns 16 weight rows and one quarter of K; every lane
-//    issues 16-byte loads of 32 consecutive FP4 codes of its row (eight loads in
-//    flight per lane), converts them with v_cvt_scalef32_pk_f16_fp4 and one
-//    packed FP16 multiply by the E4M3 scale, and feeds v_mfma_f32_16x16x32_f16
-//    with the (up to 16) activation rows as the other operand.  The activations
-//    are dequantized once per workgroup into LDS while the first weight chunks
-//    are in flight.  The four K quarters are summed in LDS in a fixed order
+//    matrix, one workgroup per 32 weight rows, each wave one interleaved
+//    eighth of K; every lane issues 16-byte loads of 32 consecutive FP4 codes
+//    of its row, converts them with v_cvt_scalef32_pk_f16_fp4 and one packed
+//    FP16 multiply by the E4M3 scale, and feeds v_mfma_f32_16x16x32_f16 with
+//    the (up to 16) activation rows as the other operand.  Each wave loads
+//    and stages the activations of its own K slice through a private LDS
+//    region, in order with its weights, so no workgroup barrier precedes the
+//    MFMAs; the eight K slices are summed in LDS in a fixed order
 //    (deterministic).
-//  * gemm_wide (larger B, prefill, K % 64 == 0): a prologue kernel writes the
-//    normalized FP16 activations once; the main kernel computes 128 x 512
-//    output tiles with 8 waves (128 x 64 each, v_mfma_f32_32x32x16_f16),
-//    streaming FP16 activations, packed FP4 weight codes and E4M3 bytes from
-//    global memory straight into four LDS stages; weights are dequantized in
-//    registers right before each MFMA.  gemm_tiled (256 x 256 tiles, register
-//    staging) serves K % 64 != 0.
+//  * gemm_wide (larger B, prefill, 16-byte weight rows, K % 64 == 0, or the
+//    pre-tiled layout): a prologue kernel writes the normalized FP16
+//    activations once; the main kernel computes 128 x 512 output tiles with 8
+//    waves (128 x 64 each, v_mfma_f32_32x32x16_f16), streaming FP16
+//    activations, packed FP4 weight codes and E4M3 bytes from global memory
+//    straight into four LDS stages; weights are dequantized in registers
+//    right before each MFMA.  gemm_tiled (256 x 256 tiles, register staging)
+//    serves the other shapes: K % 64 != 0, and weights at any alignment with
+//    K % 16 == 0 (byte loads).
 //
 // K permutation: inside each MFMA group the hardware sums over all k of the
 // instruction, so the assignment of actual k values to MFMA k-slots is free as
@@ -39,6 +43,7 @@
 #include "lds_dma.h"
 
 #include <mutex>
+#include <type_traits>
 
 namespace nvfp4 {
 
@@ -80,6 +85,25 @@ __device__ __forceinline__ v8h dequant8_act(uint32_t codes, float c) {
   return r;
 }
 
+// E4M3 bytes 0 and 1 of a word -> two FP16 values (every E4M3 value is exact
+// in FP32 and in FP16).
+__device__ __forceinline__ v2h e4m3_pair_f16(uint32_t word) {
+  const v2f f = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
+  return v2h{(_Float16)f.x, (_Float16)f.y};
+}
+
+// Eight FP4 codes times an FP16 scale pair {s, s}.
+__device__ __forceinline__ v8h dequant8_f16x2(uint32_t codes, v2h s2) {
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s2;
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * s2;
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * s2;
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * s2;
+  v8h r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
 // E4M3 byte 0 / byte 1 of a word -> FP16 (every E4M3 value is exact in FP16).
 __device__ __forceinline__ _Float16 e4m3_b0_f16(uint32_t word) {
   return (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)word, 0);
@@ -104,6 +128,15 @@ __device__ __forceinline__ uint4 load_codes32_bytes(const uint8_t* p, bool full)
   return r;
 }
 
+// 8 bytes at a 4-byte aligned address (one dwordx2 load), or by byte loads.
+typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
+__device__ __forceinline__ u32x2 load_u32x2_a4(const uint8_t* p) {
+  return *reinterpret_cast<const u32x2_a4*>(p);
+}
+__device__ __forceinline__ u32x2 load_u32x2_bytes(const uint8_t* p) {
+  return u32x2{load_u32_bytes(p), load_u32_bytes(p + 4)};
+}
+
 // Weight operand layouts of the GEMM kernels.
 constexpr int kWPlain = 0;   // [N, K/2] codes, 16-byte aligned rows (K % 32 == 0)
 constexpr int kWTiled = 1;   // the pre-tiled layout
@@ -112,199 +145,246 @@ constexpr int kWBytes = 2;   // [N, K/2] codes at any alignment, K % 16 == 0 (by
 // ------------------------------------------------------------ skinny (decode)
 
 constexpr int kSkThreads = 512;   // 8 waves
-constexpr int kSkNsub = 2;        // 16-row subtiles per workgroup
-constexpr int kSkKs = 4;          // K quarters per workgroup
-constexpr int kSkRows = 16 * kSkNsub;
-constexpr int kSkPF = 8;          // 128-k chunks loaded per round per wave
-constexpr int kSkItems = 16;      // activation items (8 codes) per thread
-constexpr int kSkEarly = 5;       // weight chunks loaded before the activation prologue
-constexpr size_t kSkRedBytes = (size_t)kSkKs * kSkRows * 16 * sizeof(float);
+constexpr int kSkWaves = kSkThreads / 64;
+constexpr int kSkRows = 32;       // weight rows per workgroup: two 16-row MFMA groups
+constexpr int kSkPF = 4;          // 128-k chunks per round (all loads of a round in flight)
+constexpr int kSkHalves = 2;      // per half round: one activation load group and one 2^e per row
+constexpr int kSkHC = kSkPF / kSkHalves;
+constexpr int kSkPitch = kSkPF * 128 + 8;        // halves per staged activation row
+constexpr int kSkRedPitch = kSkRows * 16 + 4;    // floats per wave in the K-slice reduction
 
-// One workgroup = 8 waves = 2 sixteen-row weight subtiles x 4 K quarters.
-// Order of work, chosen against the memory latency chain of one workgroup:
-//  1. every thread issues the loads of its activation items (a few codes +
-//     combined scales; shared by all workgroups, so they hit L2), the global
-//     weight scale, and the weight loads of the first kSkEarly chunks;
-//  2. row maxima of the combined scales (wave reduction + LDS integer max),
-//     the per-row power of two, and the FP16 activations in LDS -- three
-//     barriers, which wait only for the issue of the few loads above (a wave
-//     whose weight loads are throttled by HBM would hold every barrier);
-//  3. the remaining weight loads of the round, then MFMAs chunk by chunk as the
-//     data arrives (in-order load counter).  The first round is straight-line
-//     code: inside a loop the compiler drained every outstanding load at the
-//     loop head, so the later chunks' loads waited a full memory latency;
-//  4. the four K quarters are summed in LDS in a fixed order.
+// Dynamic LDS of the skinny kernel for IPL activation items per lane: per wave
+// a stage of 4 IPL + 1 rows x kSkPitch halves and as many FP32 powers of two
+// (the K-slice reduction reuses the stages after a barrier).
+constexpr size_t skinny_lds_bytes(int ipl) {
+  return (size_t)kSkWaves * (size_t)(4 * ipl + 1) * (kSkPitch * 2 + 4 * kSkHalves);
+}
+static_assert(skinny_lds_bytes(1) >= (size_t)kSkWaves * kSkRedPitch * 4, "reduction fits the stages");
+
+// One workgroup = 32 weight rows x all of K; wave w owns the 128-k chunks
+// [w nch / 8, (w+1) nch / 8) for both 16-row groups, in rounds of kSkPF
+// chunks.  A round:
+//  1. issues its loads half round by half round: the half's activation items
+//     (IPL per lane, each 16 codes of one row and their FP32 combined scale;
+//     the 16 lanes of a row cover the half's 2 x 128 k), then the half's
+//     weight tiles.  With the in-order load counter, each half's activations
+//     arrive before its weights and the first half is processed while the
+//     second streams in -- no workgroup barrier and no prologue precede the
+//     MFMAs;
+//  2. per half, the row maximum of the combined scales (DPP over the 16-lane
+//     row holding the row's items) gives a power of two 2^e per row; the
+//     items are dequantized as q * (c 2^-e), rounded
+//     once to FP16 (|value| < 12), into a stage in the wave's own LDS region,
+//     read back in MFMA layout (LDS operations of one wave run in order, so
+//     no barrier);
+//  3. per chunk the weights are dequantized in registers (e2m1 * e4m3 is exact
+//     in FP16) and feed one v_mfma_f32_16x16x32_f16 chain per row group over
+//     the half; the chain result times 2^e is added to the FP32 total.
+// At the end the eight K slices are summed in LDS in a fixed order.
+// Rounds that lie inside K and the wave's range run without any per-item
+// validity selects and with constant address offsets; the last partial round
+// re-loads valid addresses and zeroes what lies outside.
 // A4: activation codes 4-byte aligned (dword loads), else byte loads.
-// NI: activation items (units of eight codes) per thread, >= B * ceil(K/8 / 512).
-// WL = kWTiled: the weights are in the pre-tiled layout (nvfp4_pretile_weight):
-// each wave-load of 16 rows x 128 k is one contiguous KiB (codes) / 128 B (E4M3
-// bytes) instead of 16 row segments.  WL = kWBytes: the scalar path for
-// weights at any alignment and K % 16 == 0: the same arithmetic on the same
-// values (bit-identical results), with byte loads, and both operands zeroed
-// for the k past the row end of a half-filled last 32-k group.
-template <bool A4, int NI, int WL>
-__global__ void __launch_bounds__(kSkThreads)
+// IPL: activation items per lane per chunk; B <= 4 * IPL.
+// WL: weight layout (kWPlain, kWTiled = pre-tiled, each wave-load of 16 rows
+// x 128 k one contiguous KiB of codes / 128 B of E4M3 bytes, kWBytes = any
+// alignment and K % 16 == 0 by byte loads, the upper 16 k of a half-filled
+// last 32-k group zero).  All three run the same arithmetic on the same
+// values: bit-identical results.
+// One workgroup per CU (256 workgroups fill the chip for N = 8192), so two
+// waves per SIMD: the registers go to loads in flight and operand buffers.
+template <bool A4, int IPL, int WL>
+__global__ void __launch_bounds__(kSkThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_skinny(const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
             const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_sf,
             const float* __restrict__ w_g, _Float16* __restrict__ y, int B, int N, int K) {
+  constexpr int R = 4 * IPL;                  // staged activation rows; row R takes the
+                                              // writes of items past row B-1
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ float rs[16];
-  __shared__ float rinv[16];
-  __shared__ uint32_t rmax[16];
-  const int pitch = K + 8;   // halves; keeps consecutive activation rows 16 B apart in bank space
-  _Float16* As = reinterpret_cast<_Float16*>(smem);
-  float* red = reinterpret_cast<float*>(smem + (((size_t)B * pitch * 2 + 15) / 16) * 16);
-
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int nsub = wave % kSkNsub, ks = wave / kSkNsub;
+  _Float16* st = reinterpret_cast<_Float16*>(smem) + (size_t)wave * (R + 1) * kSkPitch;
+  float* sexp = reinterpret_cast<float*>(smem + (size_t)kSkWaves * (R + 1) * kSkPitch * 2) +
+                wave * (R + 1) * kSkHalves;
+  float* red = reinterpret_cast<float*>(smem);   // after the last round
+
   const int r16 = lane & 15, g = lane >> 4;
-  const int nrow = blockIdx.x * kSkRows + nsub * 16 + r16;
+  const int nch = (K + 127) >> 7;
+  // this wave's chunks: chunk(m) for m < cnt
+  // interleaved chunks: waves side by side on the same 128-byte segments of
+  // plain weight rows read faster than contiguous K slices per wave (and every
+  // layout keeps the same summation order)
+  constexpr bool kInterleave = true;
+  const int cnt = kInterleave ? (wave < nch ? (nch - 1 - wave) / kSkWaves + 1 : 0)
+                              : (wave + 1) * nch / kSkWaves - wave * nch / kSkWaves;
+  const int cbase = kInterleave ? wave : wave * nch / kSkWaves;
+  auto chunk = [&](int m) { return kInterleave ? cbase + kSkWaves * m : cbase + m; };
   const int64_t kb2 = K / 2, kb16 = K / 16;
-  const int nchunks = (K + 127) >> 7;
-  if (tid < 16) rmax[tid] = 0u;
+  const int rb = r16 < B ? r16 : B - 1;       // activation row of this lane's MFMA column
 
-  // 1a. this thread's activation items: item j is unit q8 = tid + 512 i (eight
-  //     codes) of row b, (b, i) running over (0, 0), (0, 1), ..., (0, ipr-1),
-  //     (1, 0), ... (wave-uniform counters).  Loads are unconditional: items
-  //     past the last row or the row end re-load a valid unit (masked later).
-  const int per_row = K / 8;
-  const int ipr = (per_row + kSkThreads - 1) / kSkThreads;
-  uint32_t acode[NI];
-  float ascl[NI];
-  {
-    int b = 0, i = 0;
+  int nrow[2];                                // rows past N re-read row N-1 (not stored)
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int q8 = tid + kSkThreads * i;
-      const int bb = b < B ? b : B - 1;
-      const int qq = q8 < per_row ? q8 : 0;
-      const uint8_t* pa = a + (int64_t)bb * kb2 + 4 * (int64_t)qq;
-      acode[j] = A4 ? *reinterpret_cast<const uint32_t*>(pa) : load_u32_bytes(pa);
-      ascl[j] = a_scale[(int64_t)bb * kb16 + qq / 2];
-      if (++i == ipr) { i = 0; ++b; }
-    }
+  for (int rg = 0; rg < 2; ++rg) {
+    const int n = blockIdx.x * kSkRows + rg * 16 + r16;
+    nrow[rg] = n < N ? n : N - 1;
   }
-  const float gw = *w_g;
-
-  // 1b. weight loads.  Rows past N re-load row N-1 (their outputs are not
-  //     stored); chunks past the end of K re-load chunk 0 and are skipped.
-  const uint8_t* wr = w + (int64_t)(nrow < N ? nrow : N - 1) * kb2;
-  const uint8_t* sr = w_sf + (int64_t)(nrow < N ? nrow : N - 1) * kb16;
-  uint4 wc[kSkPF];
-  uint32_t wsv[kSkPF];
-  auto load_chunks = [&](int c0, int i0, int i1) {
+  // activation items: per half round (two chunks), item j of lane l is row
+  // l / 16 + 4 j, the 16 codes at k = 16 (l % 8) .. +15 of the half's chunk
+  // (l % 16) / 8 (8 B of codes, one FP32 combined scale)
+  int arow[IPL], srow[IPL];
 #pragma unroll
-    for (int i = 0; i < kSkPF; ++i) {
-      if (i < i0 || i >= i1) continue;
-      const int c = c0 + i * kSkKs;
-      if constexpr (WL == kWTiled) {
-        // tile (row group, chunk), lane order r16 + 16 g (K % 128 == 0)
-        const int64_t t = ((int64_t)(nrow < N ? nrow : N - 1) / 16 * nchunks + (c < nchunks ? c : 0)) * 64 + lane;
-        wc[i] = *reinterpret_cast<const uint4*>(w + t * 16);
-        wsv[i] = (uint32_t)*reinterpret_cast<const uint16_t*>(w_sf + t * 2);
-      } else if constexpr (WL == kWBytes) {
-        const int k0 = c * 128 + 32 * g;
-        const int k = (c < nchunks && k0 < K) ? k0 : 0;
-        const bool full = k + 16 < K;
-        wc[i] = load_codes32_bytes(wr + k / 2, full);
-        wsv[i] = (uint32_t)sr[k / 16] | (full ? (uint32_t)sr[k / 16 + 1] << 8 : 0u);
-      } else {
-        const int k0 = c * 128 + 32 * g;
-        const int k = (c < nchunks && k0 < K) ? k0 : 0;
-        wc[i] = *reinterpret_cast<const uint4*>(wr + k / 2);
-        wsv[i] = (uint32_t)*reinterpret_cast<const uint16_t*>(sr + k / 16);
-      }
-    }
-  };
-  load_chunks(ks, 0, kSkEarly);
-  __syncthreads();   // rmax cleared
+  for (int j = 0; j < IPL; ++j) {
+    const int b = (lane >> 4) + 4 * j;
+    arow[j] = b < B ? b : B - 1;
+    srow[j] = b < B ? b : R;
+  }
+  const int ich = (lane & 15) >> 3, ik = 16 * (lane & 7);
 
-  // 2. per-row power-of-two normalization: row max of the (non-negative)
-  //    combined scales as an integer max of their bits, per wave then in LDS
-  {
-    float cur = 0.0f;
-    int b = 0, i = 0;
+  v4f tot[2];
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const bool v = tid + kSkThreads * i < per_row;
-      cur = __builtin_fmaxf(cur, v ? ascl[j] : 0.0f);
-      if (i + 1 == ipr || j == NI - 1) {
-        if (b < B) {
-          const float m = wave_max_dpp(cur);
-          if (lane == 0) atomicMax(&rmax[b], __float_as_uint(m) & 0x7FFFFFFFu);
+  for (int rg = 0; rg < 2; ++rg) tot[rg] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // FULL: all kSkPF chunks of the round inside the wave's list and inside K
+  auto round = [&](int mb, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    u32x2 acode[kSkHalves][IPL];
+    float ascl[kSkHalves][IPL];
+    uint4 wc[kSkPF][2];
+    uint32_t wsv[kSkPF][2];
+    int ka[kSkHalves];
+    // 1. loads, half by half: the half's activation items, then its weight
+    //    tiles.  In a partial round, codes and scales outside the range or
+    //    past K are not read (addresses clamped to k = 0) and are zeroed below.
+#pragma unroll
+    for (int h = 0; h < kSkHalves; ++h) {
+      const int mi = mb + kSkHC * h + ich;
+      ka[h] = chunk(FULL ? mi : (mi < cnt ? mi : cnt - 1)) * 128 + ik;   // first k of the item
+#pragma unroll
+      for (int j = 0; j < IPL; ++j) {
+        const uint8_t* pa = a + (int64_t)arow[j] * kb2;
+        const float* ps = a_scale + (int64_t)arow[j] * kb16;
+        if (FULL) {
+          acode[h][j] = A4 ? load_u32x2_a4(pa + ka[h] / 2) : load_u32x2_bytes(pa + ka[h] / 2);
+          ascl[h][j] = ps[ka[h] / 16];
+        } else {
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int k = ka[h] + 8 * q < K ? ka[h] + 8 * q : 0;
+            acode[h][j][q] = A4 ? *reinterpret_cast<const uint32_t*>(pa + k / 2) : load_u32_bytes(pa + k / 2);
+          }
+          ascl[h][j] = ps[ka[h] < K ? ka[h] / 16 : 0];
         }
-        cur = 0.0f;
       }
-      if (++i == ipr) { i = 0; ++b; }
-    }
-  }
-  __syncthreads();
-  if (tid < B) {
-    const int e = row_exponent(__uint_as_float(rmax[tid]));
-    rs[tid] = __builtin_ldexpf(1.0f, e);
-    rinv[tid] = __builtin_ldexpf(1.0f, -e);
-  }
-  __syncthreads();
-  {
-    int b = 0, i = 0;
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int q8 = tid + kSkThreads * i;
-      if (b < B && q8 < per_row)
-        *reinterpret_cast<v8h*>(As + (int64_t)b * pitch + 8 * q8) = dequant8_act(acode[j], ascl[j] * rinv[b]);
-      if (++i == ipr) { i = 0; ++b; }
+      for (int ii = 0; ii < kSkHC; ++ii) {
+        const int i = kSkHC * h + ii;
+        const int c = chunk(FULL ? mb + i : (mb + i < cnt ? mb + i : cnt - 1));
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg) {
+          if constexpr (WL == kWTiled) {
+            // tile (row group, chunk), lane order r16 + 16 g (K % 128 == 0)
+            const int64_t t = ((int64_t)(nrow[rg] >> 4) * nch + c) * 64 + lane;
+            wc[i][rg] = *reinterpret_cast<const uint4*>(w + t * 16);
+            wsv[i][rg] = (uint32_t)*reinterpret_cast<const uint16_t*>(w_sf + t * 2);
+          } else {
+            const int k0 = c * 128 + 32 * g;
+            const int k = FULL ? k0 : (k0 < K ? k0 : 0);
+            const uint8_t* wr = w + (int64_t)nrow[rg] * kb2 + k / 2;
+            const uint8_t* sr = w_sf + (int64_t)nrow[rg] * kb16 + k / 16;
+            if constexpr (WL == kWBytes) {
+              const bool full = FULL || k + 16 < K;
+              wc[i][rg] = load_codes32_bytes(wr, full);
+              wsv[i][rg] = (uint32_t)sr[0] | (full ? (uint32_t)sr[1] << 8 : 0u);
+            } else {
+              wc[i][rg] = *reinterpret_cast<const uint4*>(wr);
+              wsv[i][rg] = (uint32_t)*reinterpret_cast<const uint16_t*>(sr);
+            }
+          }
+        }
+      }
+      // issue order = arrival order: keep the halves' load groups apart, and
+      // every load of the round ahead of the first use (the scheduler would
+      // otherwise reorder them or sink later loads below earlier work)
+      __builtin_amdgcn_sched_barrier(0);
     }
-  }
-  __syncthreads();
 
-  // 3. stream the weights.  Batch columns past B read row B-1 of the LDS
-  //    activations; their outputs are never stored.
-  load_chunks(ks, kSkEarly, kSkPF);
-  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  const _Float16* arow = As + (r16 < B ? r16 : B - 1) * pitch;
-  auto compute_round = [&](int c0) {
 #pragma unroll
-    for (int i = 0; i < kSkPF; ++i) {
-      const int c = c0 + i * kSkKs;
-      if (c < nchunks) {   // wave-uniform
-        const int k = c * 128 + 32 * g;
-        const bool kv = k < K;   // false only in a partial last chunk
+    for (int h = 0; h < kSkHalves; ++h) {
+      // 2. stage the half's activations, normalized per row by 2^-e; items
+      //    outside the range or past K stage zeros.  Stores are unconditional
+      //    (a branch would move the loads into it, behind a wait for all loads).
+      const bool iv = FULL || mb + kSkHC * h + ich < cnt;   // the item's chunk is in the wave's list
+#pragma unroll
+      for (int j = 0; j < IPL; ++j) {
+        const float sc = (FULL || (iv && ka[h] < K)) ? ascl[h][j] : 0.0f;
+        uint32_t code[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) code[q] = (FULL || (iv && ka[h] + 8 * q < K)) ? acode[h][j][q] : 0u;
+        const int e = row_exponent(row16_max(__builtin_fabsf(sc)));
+        const float c = sc * __builtin_ldexpf(1.0f, -e);
+        _Float16* dst = st + srow[j] * kSkPitch + 128 * (kSkHC * h + ich) + ik;
+        *reinterpret_cast<v8h*>(dst) = dequant8_act(code[0], c);
+        *reinterpret_cast<v8h*>(dst + 8) = dequant8_act(code[1], c);
+        sexp[h * (R + 1) + srow[j]] = __builtin_ldexpf(1.0f, e);   // the same value from the row's 16 lanes
+      }
+      __builtin_amdgcn_sched_barrier(0);   // staging first: it waits only for the half's activations
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+      // 3. the half's weights chunk by chunk, one MFMA chain per row group
+      v4f acc[2];
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg) acc[rg] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ii = 0; ii < kSkHC; ++ii) {
+        const int i = kSkHC * h + ii;
         v8h bf[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) bf[m] = *reinterpret_cast<const v8h*>(arow + (kv ? k : 0) + 8 * m);
-        if constexpr (WL == kWBytes) {
-          // k + 16 .. k + 31 past the row end: the LDS there is not this row
-          if (k + 16 >= K) { bf[2] = v8h{}; bf[3] = v8h{}; }
-        }
-        const _Float16 s0 = e4m3_b0_f16(wsv[i]), s1 = e4m3_b1_f16(wsv[i]);
-        const uint32_t cw[4] = {kv ? wc[i].x : 0u, kv ? wc[i].y : 0u, kv ? wc[i].z : 0u, kv ? wc[i].w : 0u};
-#pragma unroll
         for (int m = 0; m < 4; ++m)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16(cw[m], m < 2 ? s0 : s1), bf[m], acc, 0, 0, 0);
+          bf[m] = *reinterpret_cast<const v8h*>(st + rb * kSkPitch + 128 * i + 32 * g + 8 * m);
+        // weight codes past K (a partial last chunk) or of chunks past the
+        // range are zeroed; their activations are zero as well
+        const bool kv = FULL || (mb + i < cnt && chunk(mb + i) * 128 + 32 * g < K);
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg) {
+          const v2h sp = e4m3_pair_f16(wsv[i][rg]);
+          const v2h s0 = {sp[0], sp[0]}, s1 = {sp[1], sp[1]};
+          const uint32_t cw[4] = {kv ? wc[i][rg].x : 0u, kv ? wc[i][rg].y : 0u, kv ? wc[i][rg].z : 0u,
+                                  kv ? wc[i][rg].w : 0u};
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16x2(cw[m], m < 2 ? s0 : s1), bf[m], acc[rg], 0, 0, 0);
+        }
       }
+      const float es = sexp[h * (R + 1) + rb];
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tot[rg][r] += acc[rg][r] * es;
+      __builtin_amdgcn_sched_barrier(0);   // the next half's staging after this half's work
     }
   };
-  // the first round straight-line (its loads were issued above), later rounds
-  // (K > 4096) in a loop
-  compute_round(ks);
-  for (int c0 = ks + kSkPF * kSkKs; c0 < nchunks; c0 += kSkPF * kSkKs) {
-    load_chunks(c0, 0, kSkPF);
-    compute_round(c0);
-  }
 
-  // 4. sum the K quarters in a fixed order, scale, round to FP16
+  int mb = 0;
+  for (; mb + kSkPF <= cnt && (chunk(mb + kSkPF - 1) + 1) * 128 <= K; mb += kSkPF) round(mb, std::true_type{});
+  if (mb < cnt) round(mb, std::false_type{});   // wave-uniform
+
+  // sum the eight K slices in a fixed order, scale, round to FP16
+  __syncthreads();   // every wave is done with its stage
 #pragma unroll
-  for (int r = 0; r < 4; ++r) red[(ks * kSkRows + nsub * 16 + 4 * g + r) * 16 + r16] = acc[r];
+  for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave * kSkRedPitch + (rg * 16 + 4 * g + r) * 16 + r16] = tot[rg][r];
   __syncthreads();
+  const float gw = *w_g;
   for (int t = tid; t < 16 * kSkRows; t += kSkThreads) {
     const int b = t / kSkRows, nl = t % kSkRows;
     const int n = blockIdx.x * kSkRows + nl;
     if (b < B && n < N) {
-      float s = red[(0 * kSkRows + nl) * 16 + b];
+      float s = red[nl * 16 + b];
 #pragma unroll
-      for (int q = 1; q < kSkKs; ++q) s += red[(q * kSkRows + nl) * 16 + b];
-      y[(int64_t)b * N + n] = (_Float16)((s * rs[b]) * gw);
+      for (int q = 1; q < kSkWaves; ++q) s += red[q * kSkRedPitch + nl * 16 + b];
+      y[(int64_t)b * N + n] = (_Float16)(s * gw);
     }
   }
 }
@@ -312,28 +392,21 @@ gemm_skinny(const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
 typedef void (*SkinnyFn)(const uint8_t*, const float*, const uint8_t*, const uint8_t*, const float*,
                          _Float16*, int, int, int);
 
-// The instantiation with the fewest activation items per thread covering ni.
+// Activation items per lane covering B rows.
+int skinny_ipl(int B) { return B <= 4 ? 1 : (B <= 8 ? 2 : 4); }
+
 template <bool A4, int WL>
-SkinnyFn skinny_kernel_a(int ni) {
-  if (ni <= 1) return gemm_skinny<A4, 1, WL>;
-  if (ni <= 2) return gemm_skinny<A4, 2, WL>;
-  if (ni <= 4) return gemm_skinny<A4, 4, WL>;
-  if (ni <= 8) return gemm_skinny<A4, 8, WL>;
-  return gemm_skinny<A4, kSkItems, WL>;
+SkinnyFn skinny_kernel_a(int ipl) {
+  if (ipl == 1) return gemm_skinny<A4, 1, WL>;
+  if (ipl == 2) return gemm_skinny<A4, 2, WL>;
+  return gemm_skinny<A4, 4, WL>;
 }
 // The byte-load weight path uses byte loads for the activation codes too.
-SkinnyFn skinny_kernel(bool a4, int ni, int wl) {
-  if (wl == kWBytes) return skinny_kernel_a<false, kWBytes>(ni);
-  if (wl == kWTiled) return a4 ? skinny_kernel_a<true, kWTiled>(ni) : skinny_kernel_a<false, kWTiled>(ni);
-  return a4 ? skinny_kernel_a<true, kWPlain>(ni) : skinny_kernel_a<false, kWPlain>(ni);
+SkinnyFn skinny_kernel(bool a4, int ipl, int wl) {
+  if (wl == kWBytes) return skinny_kernel_a<false, kWBytes>(ipl);
+  if (wl == kWTiled) return a4 ? skinny_kernel_a<true, kWTiled>(ipl) : skinny_kernel_a<false, kWTiled>(ipl);
+  return a4 ? skinny_kernel_a<true, kWPlain>(ipl) : skinny_kernel_a<false, kWPlain>(ipl);
 }
-
-size_t skinny_lds_bytes(int64_t B, int64_t K) {
-  return (((size_t)B * (size_t)(K + 8) * 2 + 15) / 16) * 16 + kSkRedBytes;
-}
-
-// Dynamic LDS budget of the skinny kernel (its static LDS is 192 bytes).
-constexpr size_t kSkinnyDynMax = 160 * 1024 - 1024;
 
 // ------------------------------------------------------------ tiled (prefill)
 
@@ -732,10 +805,7 @@ gemm_wide(const _Float16* __restrict__ a16, const float* __restrict__ rowscale,
   }
 }
 
-bool use_skinny(int64_t B, int64_t K) {
-  const int64_t ipr = (K / 8 + kSkThreads - 1) / kSkThreads;
-  return B <= 16 && skinny_lds_bytes(B, K) <= kSkinnyDynMax && B * ipr <= kSkItems;
-}
+bool use_skinny(int64_t B) { return B <= 16; }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -744,7 +814,7 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // Workspace of the tiled paths: [FP16 activations] [row powers of two].
 size_t gemm_workspace_bytes(int64_t B, int64_t N, int64_t K) {
   (void)N;
-  if (use_skinny(B, K)) return 0;
+  if (use_skinny(B)) return 0;
   return align256((size_t)B * (size_t)K * 2) + align256((size_t)B * 4);
 }
 
@@ -777,9 +847,10 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   std::call_once(once, []() {
     for (int wl = kWPlain; wl <= kWBytes && attr_err == hipSuccess; ++wl)
       for (int a4 = 0; a4 < 2 && attr_err == hipSuccess; ++a4)
-        for (int ni = 1; ni <= kSkItems && attr_err == hipSuccess; ni *= 2)
-          attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(skinny_kernel(a4 != 0, ni, wl)),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSkinnyDynMax);
+        for (int ipl = 1; ipl <= 4 && attr_err == hipSuccess; ipl *= 2)
+          attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(skinny_kernel(a4 != 0, ipl, wl)),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)skinny_lds_bytes(ipl));
     if (attr_err == hipSuccess)
       attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled<false>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTiledLds);
@@ -794,12 +865,12 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   // 16-byte weight rows and 2-byte scale rows, else the byte-load path
   const bool w_rows16 = ((uintptr_t)g.w % 16) == 0 && (K % 32) == 0 && ((uintptr_t)g.w_sf % 2) == 0;
   const int wl = g.tiled ? kWTiled : (w_rows16 ? kWPlain : kWBytes);
-  if (use_skinny(g.B, g.K)) {
+  if (use_skinny(g.B)) {
     const unsigned grid = (unsigned)((N + kSkRows - 1) / kSkRows);
-    const int ni = B * ((K / 8 + kSkThreads - 1) / kSkThreads);
-    const SkinnyFn fn = skinny_kernel(((uintptr_t)g.a % 4) == 0, ni, wl);
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(kSkThreads), skinny_lds_bytes(B, K), s, g.a, g.a_scale,
-                       g.w, g.w_sf, g.w_g, y, B, N, K);
+    const int ipl = skinny_ipl(B);
+    const SkinnyFn fn = skinny_kernel(((uintptr_t)g.a % 4) == 0, ipl, wl);
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(kSkThreads), skinny_lds_bytes(ipl), s, g.a, g.a_scale, g.w,
+                       g.w_sf, g.w_g, y, B, N, K);
     return hipGetLastError();
   }
   unsigned char* ws = reinterpret_cast<unsigned char*>(g.workspace);
