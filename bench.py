@@ -363,7 +363,56 @@ def cpu_baseline(si, pre):
     return {"value": 2.0 * R * N * K * reps / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": "%d repetitions of the full step (%d activation rows): C-oracle per-token quantize "
                       "(1 thread) + fp64 numpy GEMM reference against the %dx%d weight, %.1f s in total"
-                      % (reps, R, N, K, dt)}
+                      % (reps, R, N, K, dt),
+            "quantizers": oracle_quant_rates(si, a), "host": host_info()}
+
+
+def host_info():
+    """Host CPU model and the cores this process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": len(os.sched_getaffinity(0)), "cpu_count": os.cpu_count()}
+
+
+def oracle_quant_rates(si, a):
+    """The C oracle's quantizer throughput in the GPU figures' byte accounting,
+    on a bounded sample of rows: one thread, then all cores of the job's share
+    (a thread pool over chunks of rows; the C call releases the GIL)."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    # every core this process may use, within the job's CPU share
+    ncores = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "16")))
+
+    def rate(x, act, want_scale, k_in, k_out, rows, threads, chunk):
+        parts = [x[i:i + chunk] for i in range(0, rows, chunk)]
+        f = lambda p: oracle.quantize(p, act, want_scale=want_scale)
+        t0 = time.perf_counter()
+        if threads == 1:
+            for p in parts:
+                f(p)
+        else:
+            with ThreadPoolExecutor(threads) as ex:
+                list(ex.map(f, parts))
+        dt = time.perf_counter() - t0
+        by = quant_bytes(rows, k_in, k_out, scale=want_scale)
+        return {"rows": rows, "threads": threads, "s": round(dt, 3), "GBps": by / dt / 1e9}
+
+    c3 = si.CONFIGS["C3"]
+    x4 = si.swiglu_input(rows=2048)
+    H = x4.shape[1] // 2
+    return {
+        "C3_act_quant": [rate(a, oracle.ACT_NONE, True, c3["K"], c3["K"], 2048, 1, 256),
+                         rate(a, oracle.ACT_NONE, True, c3["K"], c3["K"], a.shape[0], ncores, 64)],
+        "C4_swiglu_quant": [rate(x4, oracle.ACT_SWIGLU, False, 2 * H, H, 512, 1, 128),
+                            rate(x4, oracle.ACT_SWIGLU, False, 2 * H, H, x4.shape[0], ncores, 32)],
+    }
 
 
 def load_traffic():

@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import synth_inputs as si
+from quant_diagnostics import report, stats
 
 pytestmark = pytest.mark.gpu
 
@@ -130,9 +131,13 @@ def test_full_size_swiglu_sampled_rows(nv, oracle):
             g, w = g.view(np.uint32), w.view(np.uint32)
         assert np.array_equal(g, w), k
     assert np.array_equal(got["g_dec"].cpu().numpy()[rows].view(np.uint32), want["g_dec"].view(np.uint32))
-    # every row: the block holding the row maximum has scale byte 448 (0x7E)
+    # every row: the block holding the row maximum has scale byte 448 (0x7E);
+    # every normal-scale block of the whole output holds a +-6 code
     sf = got["sf"].cpu().numpy()
     assert np.all(sf.max(axis=1) == 0x7E)
+    d = stats(got["codes"].cpu().numpy(), sf)
+    report("C4 SwiGLU [8192, 14336] (GPU, all rows)", d)
+    assert d["normal_blocks_without_max_code"] == 0 and d["nonzero_rows_without_448"] == 0
 
 
 def test_full_size_prefill_activations_sampled_rows(nv, oracle):
@@ -147,6 +152,9 @@ def test_full_size_prefill_activations_sampled_rows(nv, oracle):
         if g.dtype == np.float32:
             g, w = g.view(np.uint32), w.view(np.uint32)
         assert np.array_equal(g, w), k
+    d = stats(got["codes"].cpu().numpy(), got["sf"].cpu().numpy())
+    report("C3 activations [4096, 8192] (GPU, all rows)", d)
+    assert d["normal_blocks_without_max_code"] == 0 and d["nonzero_rows_without_448"] == 0
 
 
 def test_deterministic_and_concurrent_streams(nv, oracle):
