@@ -28,9 +28,9 @@ import pytest
 import torch
 
 import synth_inputs as si
+from gemm_checks import TOL, offset_view, refs, row_checks
 
 pytestmark = pytest.mark.gpu
-TOL = 1e-3
 
 
 @pytest.fixture(scope="module")
@@ -55,40 +55,6 @@ def _quantize_groups(oracle, x, group_rows, act=0, want_scale=True):
     return out
 
 
-def _row_checks(y, ref, absref, K, act_rounding):
-    """Relative Frobenius error <= TOL in every row, and every element within
-    the bound the arithmetic allows:
-        |y - ref| <= 2^-10 |ref| + 2^-25 + (act_rounding + K 2^-24) (|A| |W|^T)
-    -- the FP16 output rounding (relative 2^-11, with slack for the fp32
-    epilogue; absolute 2^-25 for outputs in FP16's subnormal range), the one
-    rounding of each activation operand (2^-11 relative for the NVFP4 path's
-    FP16 operand, 0 for MXFP4's exact FP4 operand) and the worst-case error
-    of an fp32 sum of K products.  A wrong element or tile breaks it."""
-    y = np.asarray(y, np.float64)
-    num = np.linalg.norm(y - ref, axis=1)
-    den = np.linalg.norm(ref, axis=1)
-    rel = num / np.where(den > 0, den, 1.0)
-    assert rel.max() <= TOL, (int(rel.argmax()), float(rel.max()))
-    err = np.abs(y - ref)
-    out_round = 2.0 ** -10 * np.abs(ref) + 2.0 ** -25
-    bound = out_round + (act_rounding + K * 2.0 ** -24) * absref
-    bad = err > bound
-    if bad.any():
-        # what the failing elements needed beyond the output rounding, per |A| |W|^T
-        need = (err - out_round) / np.where(absref > 0, absref, 1.0)
-        i = np.unravel_index(np.argmax(need), need.shape)
-        raise AssertionError("%d elements beyond the bound; first %s; largest (err - output rounding)/absref = %.3e "
-                             "at %s (err %.3e, ref %.3e, absref %.3e); bound factor %.3e"
-                             % (int(bad.sum()), np.argwhere(bad)[:3].tolist(), float(need[i]), i,
-                                float(err[i]), float(ref[i]), float(absref[i]), act_rounding + K * 2.0 ** -24))
-    return float(rel.max())
-
-
-def _refs(A, W):
-    """fp64 A . W^T and |A| . |W|^T."""
-    return A @ W.T, np.abs(A) @ np.abs(W).T
-
-
 # ---------------------------------------------------------------- full C3
 
 @pytest.fixture(scope="module")
@@ -98,7 +64,7 @@ def c3(oracle):
     qw = oracle.quantize(w, group_rows=w.shape[0], want_scale=False)
     A = oracle.dequant_act(qa["codes"], qa["scale"])
     W = oracle.dequant_weight(qw["codes"], qw["sf"], qw["g_dec"][0])
-    ref, absref = _refs(A, W)
+    ref, absref = refs(A, W)
     del A, W
     return dict(a=a, w=w, qa=qa, qw=qw, ref=ref, absref=absref)
 
@@ -130,7 +96,7 @@ def test_c3_gemm_every_row(nv, oracle, c3, layout):
     torch.cuda.synchronize()
     yh = y.cpu().double().numpy()
     assert np.all(np.isfinite(yh))
-    _row_checks(yh, c3["ref"], c3["absref"], c3["a"].shape[1], 2.0 ** -11)
+    row_checks(yh, c3["ref"], c3["absref"], c3["a"].shape[1], 2.0 ** -11)
     assert oracle.rel_fro(yh, c3["ref"]) <= TOL
 
 
@@ -142,11 +108,11 @@ def test_tile_order_shape_every_row(nv, oracle, K):
     d = si.random_nvfp4_operands(B, N, K, seed=K)
     dev = "cuda"
     t = {k: torch.from_numpy(v).to(dev) for k, v in d.items()}
-    ref, absref = _refs(oracle.dequant_act(d["a_codes"], d["a_scale"]),
+    ref, absref = refs(oracle.dequant_act(d["a_codes"], d["a_scale"]),
                         oracle.dequant_weight(d["w_codes"], d["w_sf"], d["w_g"][0]))
     y = nv.gemm(t["a_codes"], t["a_scale"], t["w_codes"], t["w_sf"], t["w_g"])
     torch.cuda.synchronize()
-    _row_checks(y.cpu().double().numpy(), ref, absref, K, 2.0 ** -11)
+    row_checks(y.cpu().double().numpy(), ref, absref, K, 2.0 ** -11)
     if K % 128 == 0:
         wt = nv.pretile_weight(t["w_codes"], t["w_sf"])
         y2 = nv.gemm_pretiled(t["a_codes"], t["a_scale"], wt, t["w_g"])
@@ -164,9 +130,9 @@ def test_mx_tile_order_shape_every_row(nv, oracle):
     w = nv.mx_tile(t(d["w_codes"]), t(d["w_sf"]))
     y = nv.mx_gemm(a, t(d["a_g"]), w, t(d["w_g"]))
     torch.cuda.synchronize()
-    ref, absref = _refs(oracle.dequant_mx(d["a_codes"], d["a_sf"], d["a_g"]),
+    ref, absref = refs(oracle.dequant_mx(d["a_codes"], d["a_sf"], d["a_g"]),
                         oracle.dequant_mx(d["w_codes"], d["w_sf"], np.float32(d["w_g"][0])))
-    _row_checks(y.cpu().double().numpy(), ref, absref, K, 0.0)
+    row_checks(y.cpu().double().numpy(), ref, absref, K, 0.0)
 
 
 # ---------------------------------------------------------------- weights as benchmarked
@@ -197,21 +163,12 @@ def test_c5_expert_weights_quantize_bit_exact(nv, oracle, which):
 
 # ---------------------------------------------------------------- boundary paths
 
-def _offset_view(t: torch.Tensor, offset: int) -> torch.Tensor:
-    """The same values at `offset` bytes past a fresh allocation."""
-    nbytes = t.numel() * t.element_size()
-    buf = torch.empty(nbytes + 64, dtype=torch.uint8, device=t.device)
-    v = buf[offset:offset + nbytes]
-    v.copy_(t.contiguous().view(torch.uint8).reshape(-1))
-    return v.view(t.dtype).view(t.shape)
-
-
 @pytest.mark.parametrize("B,N,K", [(1, 96, 256), (8, 8192, 4096), (13, 64, 528)])
 def test_decode_activation_codes_at_2_byte_offset(nv, oracle, B, N, K):
     d = si.random_nvfp4_operands(B, N, K, seed=B + K)
     t = {k: torch.from_numpy(v).cuda() for k, v in d.items()}
     y0 = nv.gemm(t["a_codes"], t["a_scale"], t["w_codes"], t["w_sf"], t["w_g"])
-    a2 = _offset_view(t["a_codes"], 2)
+    a2 = offset_view(t["a_codes"], 2)
     assert a2.data_ptr() % 4 == 2
     y1 = nv.gemm(a2, t["a_scale"], t["w_codes"], t["w_sf"], t["w_g"])
     torch.cuda.synchronize()
@@ -227,7 +184,7 @@ def test_misaligned_weights_bit_identical(nv, oracle, B, N, K):
     d = si.random_nvfp4_operands(B, N, K, seed=N + K)
     t = {k: torch.from_numpy(v).cuda() for k, v in d.items()}
     y0 = nv.gemm(t["a_codes"], t["a_scale"], t["w_codes"], t["w_sf"], t["w_g"])
-    w1, s1 = _offset_view(t["w_codes"], 1), _offset_view(t["w_sf"], 3)
+    w1, s1 = offset_view(t["w_codes"], 1), offset_view(t["w_sf"], 3)
     y1 = nv.gemm(t["a_codes"], t["a_scale"], w1, s1, t["w_g"])
     torch.cuda.synchronize()
     assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
@@ -247,7 +204,7 @@ def test_k_multiple_of_16_only(nv, oracle, B, N, K, offset):
     t = lambda v: torch.from_numpy(v).cuda()
     wc, ws = t(qw["codes"]), t(qw["sf"])
     if offset:
-        wc, ws = _offset_view(wc, offset), _offset_view(ws, offset)
+        wc, ws = offset_view(wc, offset), offset_view(ws, offset)
     y = nv.gemm(t(qa["codes"]), t(qa["scale"]), wc, ws, t(qw["g_dec"]))
     torch.cuda.synchronize()
     ref = oracle.gemm_ref(qa["codes"], qa["scale"], qw["codes"], qw["sf"], qw["g_dec"][0])
@@ -263,7 +220,7 @@ def test_external_weight_matches_oracle_k_multiple_of_16(nv, oracle):
     qa = oracle.quantize(a)
     qw = oracle.quantize(w, group_rows=N, want_scale=False)
     t = lambda v: torch.from_numpy(v).cuda()
-    wc, ws = _offset_view(t(qw["codes"]), 5), _offset_view(t(qw["sf"]), 1)
+    wc, ws = offset_view(t(qw["codes"]), 5), offset_view(t(qw["sf"]), 1)
     nv.register_weight(77, wc, ws)
     try:
         y = nv.gemm_external(t(qa["codes"]), t(qa["scale"]), 77, N, t(qw["g_dec"]))
@@ -281,7 +238,7 @@ def test_per_tensor_quantize_at_2_byte_offset(nv, oracle, dtype):
     x = si.normal_f32((rows, k), 0.5, 85, 0)
     x = torch.from_numpy(x).to(dtype)
     q = oracle.quantize(x, group_rows=rows)
-    xg = _offset_view(x.cuda(), 2)
+    xg = offset_view(x.cuda(), 2)
     assert xg.data_ptr() % 16 == 2
     g = nv.quantize(xg, group_rows=rows)
     q2 = oracle.quantize(x, group_rows=rows // 4)
