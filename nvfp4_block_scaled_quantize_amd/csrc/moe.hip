@@ -311,18 +311,17 @@ __device__ __forceinline__ v8h dequant8_w(uint32_t codes, _Float16 s16) {
 }
 
 // Expert FFN layer.  A unit of work is (expert e, tile of 256 weight rows,
-// pass of up to 160 of the expert's tokens); an expert with more tokens is
+// pass of up to kFwTok of the expert's tokens); an expert with more tokens is
 // cut into balanced passes.  Workgroup (x, e, z) takes passes z, z +
 // gridDim.z, ... and, within each pass, R consecutive row tiles streamed back
-// to back (R > 1 when experts x tiles exceeds the compute units, so that the
-// units split evenly over them).  8 waves x one 32-row
-// v_mfma_f32_32x32x16_f16 tile, five 32-token tiles.  K goes in 128-k
-// chunks; lane (row r, half h) owns the 64 k at 64 h of a chunk: two 16-byte
-// code loads and one 4-byte load of its four E4M3 bytes, issued three chunks
-// ahead (across row tiles) into registers and used as loaded (no widening or
-// packing that would make the compiler wait for them early).  MFMA m of a
-// chunk takes k = 64 h + 8 m .. + 7 from both operands.  The FP16 activations
-// of a chunk are loaded two chunks ahead into registers and written to LDS
+// to back (R > 1 when the units number four or more per workgroup slot).
+// 8 waves x one 32-row v_mfma_f32_32x32x16_f16 tile, kFwTT 32-token tiles.
+// K goes in 128-k chunks; lane (row r, half h) owns the 64 k at 64 h of a
+// chunk: two 16-byte code loads and one 4-byte load of its four E4M3 bytes,
+// issued three chunks ahead (across row tiles) into registers and used as
+// loaded (no widening or packing that would make the compiler wait for them
+// early).  MFMA m of a chunk takes k = 64 h + 8 m .. + 7 from both operands.  The FP16 activations
+// of a chunk are loaded three chunks ahead into registers and written to LDS
 // one chunk ahead.  Loads are issued in the order they are needed and the
 // chunk barrier waits for LDS traffic only, so each wait covers just what the
 // next step uses.  Requires K % 64 == 0.
@@ -660,12 +659,15 @@ size_t moe_workspace_bytes(int tokens, int experts, int top_k, int hidden, int i
          align256(P * fc1_tiles(inter) * 4) + align256(P * inter * 2) + align256(P * hidden * 4);
 }
 
-// Row tiles per workgroup: enough that the (expert, row tile) units of a
-// layer split evenly over the compute units when there are more of them.
+// Row tiles per workgroup.  One while the (expert, row tile) units number
+// less than four per workgroup slot: smaller units finish the layer in fewer
+// unit-lengths (for the 64-expert, 2048-row fc2 layer, 512 units of one tile
+// beat 256 of two by ~3 us); beyond that, R tiles streamed back to back share
+// one prologue.
 static int tiles_per_wg(int experts, int n, int num_cus) {
   const int units = experts * ((n + kFwRows - 1) / kFwRows);
   const int slots = num_cus * kFwPerCU;
-  int r = slots > 0 ? units / slots : 1;
+  int r = slots > 0 ? units / (2 * slots) : 1;
   return r < 1 ? 1 : (r > 8 ? 8 : r);
 }
 
