@@ -228,8 +228,9 @@ int32_t nvfp4_gemm_external(const uint8_t* a, const float* a_scale, int32_t reso
  * by their sum when norm_topk_prob, times routed_scaling.
  * Requires experts % n_group == 0, 1 <= topk_group <= n_group,
  * 1 <= top_k <= topk_group * experts / n_group, top_k <= 16, experts <= 256,
- * hidden % 64 == 0, inter % 64 == 0, inter <= 8192, tokens <= 2^24; x, w1, w2 16-byte
- * aligned, out 8-byte aligned, block scales 2-byte aligned (EINVAL otherwise).
+ * hidden % 64 == 0, inter % 64 == 0, inter <= 8192, hidden * inter <= 2^31,
+ * tokens <= 2^24; x, w1, w2 16-byte aligned, out 8-byte aligned, block scales
+ * 4-byte aligned (EINVAL otherwise).
  */
 int32_t nvfp4_moe_w4a16(const float* router_logits, const float* correction_bias, const void* x,
                         const uint8_t* w1, const uint8_t* w1_sf, const float* w1_g,

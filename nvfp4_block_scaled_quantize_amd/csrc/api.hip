@@ -315,14 +315,15 @@ static int32_t moe_check(const float* router_logits, const float* correction_bia
   if (topk_group < 1 || topk_group > n_group || top_k < 1 || top_k > 16 ||
       top_k > topk_group * gsize)
     return NVFP4_EINVAL;
-  if (hidden <= 0 || inter <= 0 || hidden % 64 != 0 || inter % 64 != 0 || inter > 8192)
+  if (hidden <= 0 || inter <= 0 || hidden % 64 != 0 || inter % 64 != 0 || inter > 8192 ||
+      (int64_t)hidden * inter > (int64_t(1) << 31))
     return NVFP4_EINVAL;
   if (tokens == 0) return NVFP4_OK;
   if (!router_logits || !correction_bias || !x || !w1 || !w1_sf || !w1_g || !w2 || !w2_sf ||
       !w2_g || !out)
     return NVFP4_EINVAL;
   if (((uintptr_t)x % 16) != 0 || ((uintptr_t)out % 8) != 0 || ((uintptr_t)w1 % 16) != 0 ||
-      ((uintptr_t)w2 % 16) != 0 || ((uintptr_t)w1_sf % 2) != 0 || ((uintptr_t)w2_sf % 2) != 0 ||
+      ((uintptr_t)w2 % 16) != 0 || !aligned4(w1_sf) || !aligned4(w2_sf) ||
       !aligned4(router_logits) || !aligned4(correction_bias) || !aligned4(w1_g) || !aligned4(w2_g))
     return NVFP4_EINVAL;
   return NVFP4_OK;

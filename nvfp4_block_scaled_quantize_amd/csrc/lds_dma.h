@@ -35,5 +35,11 @@ __device__ __forceinline__ void dma4(const void* sbase, uint32_t vofs, uint32_t 
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
                :: "s"(lds), "v"(vofs), "s"(sbase) : "memory", "m0");
 }
+// The same 16-byte copy from a full 64-bit address per lane (gathers of rows
+// that share no base within 4 GiB).
+__device__ __forceinline__ void dma16_at(const void* gaddr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds), "v"(gaddr) : "memory", "m0");
+}
 
 }  // namespace nvfp4

@@ -13,27 +13,31 @@
 //  2. lists      : one workgroup per expert writes the pairs (token, rank)
 //                  routed to it, in pair order, and their count.
 //  3. fc1        : grid (inter/256 row tiles, experts, token passes), 8 waves
-//                  x 32 weight rows, v_mfma_f32_32x32x16_f16.  Weights are
-//                  dequantized in registers (exact in FP16) and loaded three
-//                  128-k chunks ahead; the expert's tokens are gathered from x
-//                  three chunks ahead and staged in LDS, in balanced passes of
-//                  at most 64 tokens (an expert with more tokens spreads over
-//                  several workgroups).  h = relu(x . W1^T * g1)^2 is stored
-//                  as FP16 scaled by 2^-et per (pair, 256-row tile), et the
-//                  exponent of the tile's largest h; the pair's overall
-//                  largest h is an integer max of fp32 bits (order
+//                  = 4 groups of 64 weight rows x 2 token halves,
+//                  v_mfma_f32_32x32x16_f16.  Per 128-k stage the tile's FP4
+//                  codes and E4M3 bytes and the expert's FP16 token rows are
+//                  copied global -> LDS by global_load_lds, two stages ahead;
+//                  weights are dequantized in registers (exact in FP16).
+//                  Passes hold up to 128 tokens (an expert with more spreads
+//                  over several workgroups).  h = relu(x . W1^T * g1)^2 is
+//                  stored as FP16 scaled by 2^-et per (pair, 256-row tile),
+//                  et the exponent of the tile's largest h; the pair's
+//                  overall largest h is an integer max of fp32 bits (order
 //                  independent).
-//  4. fc2        : grid (hidden/256 row tiles, experts, token passes).  Same
-//                  structure on h, each tile rescaled by 2^(et - e) while
-//                  staged (e = exponent of the pair's largest h, so no pair
-//                  can overflow FP16); o = h . W2^T * g2 * 2^e in fp32 per
-//                  pair.
+//  4. fc2        : grid (hidden/512 row tiles, experts, token passes of up to
+//                  64), 8 waves of 64 rows.  Same structure on h; the products
+//                  of each 256-k range (one fc1 tile) are accumulated apart and
+//                  folded into the total with the factor 2^(et - e), e =
+//                  exponent of the pair's largest h; o = total * g2 * 2^e in
+//                  fp32 per pair.
 //  5. combine    : out[t] = sum_j w[t,j] * o[t*top_k + j] in rank order, FP16.
 #include "device_common.h"
 #include "internal.h"
+#include "lds_dma.h"
 #include "../../include/nvfp4_mi355x.h"
 
 #include <mutex>
+#include <type_traits>
 
 // Fixed device scratch of nvfp4_moe_w4a16_noalloc, for callers that cannot
 // allocate.  Each GPU the library runs on holds its own copy until the
@@ -48,22 +52,8 @@ namespace {
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Expert FFN kernels (moe_fc_wide below): work split and staging.
-constexpr int kFwThreads = 512;
-constexpr int kFwRows = 256;              // weight rows per tile (32 per wave)
-constexpr int kFwKC = 128;                // k per chunk
-constexpr int kFwTT = 2;                  // 32-token MFMA tiles per pass
-constexpr int kFwTok = 32 * kFwTT;        // tokens per pass at most
-constexpr int kFwPitch = kFwKC + 8;       // halves per staged token row (+16 B skew)
-constexpr int kFwVec = kFwTok * kFwKC / 8 / kFwThreads;   // staged 8-element vectors per thread
-constexpr int kFwRowThreads = kFwKC / 8;  // threads staging one token row of a chunk
-constexpr int kFwSlotsPerVec = kFwThreads / kFwRowThreads;   // token slots per staged vector index
-constexpr int kFwWBuf = 4;                // weight register buffers (loads three chunks ahead)
-constexpr int kFwMaxZ = 1024;             // grid z (more passes handled in a loop)
-constexpr int kFwMaxT1 = 8192 / kFwRows;  // fc1 row tiles (inter <= 8192)
-constexpr int kFwPerCU = 512 / kFwThreads;   // workgroups resident per compute unit
-static_assert(kFwVec * kFwSlotsPerVec == kFwTok, "staging covers the pass's token slots");
-static_assert(kFwRows == 32 * (kFwThreads / 64), "one 32-row MFMA tile per wave");
+// fc1 row tiles: the granularity of the per-tile exponents of h (etile)
+constexpr int kFc1Rows = 128;
 
 struct MoeWs {
   int32_t* ids;      // [P] expert of each pair
@@ -77,7 +67,7 @@ struct MoeWs {
   float* o;          // [P, hidden]
 };
 
-int fc1_tiles(int inter) { return (inter + kFwRows - 1) / kFwRows; }
+int fc1_tiles(int inter) { return (inter + kFc1Rows - 1) / kFc1Rows; }
 
 MoeWs carve(void* base, int T, int E, int P, int hidden, int inter) {
   unsigned char* p = reinterpret_cast<unsigned char*>(base);
@@ -310,326 +300,380 @@ __device__ __forceinline__ v8h dequant8_w(uint32_t codes, _Float16 s16) {
   return r;
 }
 
-// Expert FFN layer.  A unit of work is (expert e, tile of 256 weight rows,
-// pass of up to kFwTok of the expert's tokens); an expert with more tokens is
-// cut into balanced passes.  Workgroup (x, e, z) takes passes z, z +
-// gridDim.z, ... and, within each pass, R consecutive row tiles streamed back
-// to back (R > 1 when the units number four or more per workgroup slot).
-// 8 waves x one 32-row v_mfma_f32_32x32x16_f16 tile, kFwTT 32-token tiles.
-// K goes in 128-k chunks; lane (row r, half h) owns the 64 k at 64 h of a
-// chunk: two 16-byte code loads and one 4-byte load of its four E4M3 bytes,
-// issued three chunks ahead (across row tiles) into registers and used as
-// loaded (no widening or packing that would make the compiler wait for them
-// early).  MFMA m of a chunk takes k = 64 h + 8 m .. + 7 from both operands.  The FP16 activations
-// of a chunk are loaded three chunks ahead into registers and written to LDS
-// one chunk ahead.  Loads are issued in the order they are needed and the
-// chunk barrier waits for LDS traffic only, so each wait covers just what the
-// next step uses.  Requires K % 64 == 0.
+// Expert FFN layers (fc1, fc2).  A unit of work is (expert e, tile of 128
+// weight rows, pass of up to 64 of the expert's tokens); an expert with more
+// tokens is cut into balanced passes.  Workgroups are small (four waves, at
+// most 80 KiB of LDS), so two run on each compute unit and the hardware
+// dispatcher spreads the many short units evenly; the units of one expert
+// are dispatched next to each other on one XCD (its activations, and for
+// several passes its weight rows, are then read from that XCD's L2).
+// Wave w computes the weight rows 32 w .. 32 w + 31 of the tile
+// (v_mfma_f32_32x32x16_f16, weights as the A operand, dequantized in
+// registers -- exact in FP16) for every 32-token tile of the pass.
+//
+// K goes in 64-k stages copied global -> LDS by global_load_lds into two
+// rings: waves 0-1 copy the weights (FP4 codes 32 B and E4M3 bytes 4 B per
+// row and stage) through an 8-stage ring whose first seven stages are
+// issued before the token count is read; waves 2-3 gather the FP16 token
+// rows (128 B per token and stage; 64-bit addresses) through an 8-stage ring
+// for one token tile, 4 for two.  Each wave's copies are the same for every
+// stage, so its vector-memory counter waits are exact; one barrier per stage
+// publishes both.  LDS layouts (16 consecutive lanes of an operand read hit
+// 16 distinct bank groups, and 8 lanes 8):
+//   codes: 32 B per row, piece j of row r at j ^ (((r >> 2) ^ (r >> 3)) & 1);
+//   E4M3 bytes: 4 B per row;
+//   activations: 128 B per token slot, piece j of slot s at (j + rot(s)) mod
+//   8, rot(s) = s + (s / 8) mod 4 (the same for slots s and s + 32) -- a
+//   lane's four pieces of a stage are its slot base plus a constant, minus
+//   128 B past the wrap.
+// Lane (row r32, half h) owns the 32 k at 32 h of a stage: MFMA m of a stage
+// takes k = 32 h + 8 m .. + 7 from both operands.  Requires K % 64 == 0,
+// N % 64 == 0 and N K / 2 < 2^32.
 // FC = 1: act = x [T, K] (row = token).  out = h [P, N] FP16 with, per pair
-//         and row tile, h scaled by 2^-et (et = exponent of the tile's
+//         and 128-row tile, h scaled by 2^-et (et = exponent of the tile's
 //         largest h, stored in etile [P, nt1]); pmax[p] = largest h (fp32
 //         bits, integer max: order independent).
-// FC = 2: act = h [P, K]; staging rescales each 256-k tile by 2^(et - e),
-//         e = exponent of pmax[p], so the pair's values share one scale and
-//         none can overflow FP16.  out = o [P, N] fp32 = h . W^T * g * 2^e.
-
-
-template <int V> struct IntC { static constexpr int value = V; };
-
-struct WChunk {
-  uint4 q0, q1;     // 64 codes
-  uint32_t sc;      // their four E4M3 block scales
-};
-
+// FC = 2: act = h [P, K].  The activation fragments of each 128-k range (one
+//         fc1 row tile) are multiplied by 2^(et - e) in FP16 before the
+//         MFMA, e = exponent of pmax[p], so the pair's values share one scale
+//         and none can overflow FP16 (values below 2^-24 of the pair's
+//         largest h flush to zero).  out = o [P, N] fp32 = acc * g * 2^e.
+constexpr int kMfThreads = 256;            // four waves
+constexpr int kMfRows = 128;               // weight rows per tile (32 per wave)
+constexpr int kMfKC = 64;                  // k per stage
+constexpr int kMfMaxT = 2;                 // 32-token tiles per pass
+constexpr int kMfTok = 32 * kMfMaxT;       // tokens per pass at most
+constexpr int kMfCodeB = kMfRows * kMfKC / 2;        // 4096
+constexpr int kMfWB = kMfCodeB + kMfRows * kMfKC / 16;   // codes + E4M3 bytes per stage
+constexpr int kMfTileB = 32 * kMfKC * 2;   // activations of one token tile per stage
+constexpr int kMfWBufs = 5;                // weight ring
+constexpr int kMfABufs1 = 6, kMfABufs2 = 3;   // activation ring for one / two token tiles
+constexpr int kMfMaxT1 = 8192 / kMfRows;   // fc1 row tiles (inter <= 8192)
+constexpr int kMfMaxZ = 1024;              // passes in the grid (more handled in a loop)
+constexpr int kMfWOps = 3;                 // weight copies per copying thread and stage
+static_assert(kMfABufs1 * kMfTileB == kMfABufs2 * 2 * kMfTileB, "one activation ring size");
+static_assert(kMfCodeB == 2 * 16 * 128 && kMfRows * 4 == 4 * 128, "weight copies: waves 0-1");
 
 __device__ __forceinline__ int exponent_of(uint32_t bits) {
   return bits == 0u ? 0 : (int)((bits >> 23) & 0xFFu) - 127;
 }
 
+// s_waitcnt vmcnt(n) for a run-time n in [0, 23] (larger n: 23, which waits
+// at least as long).
+__device__ __forceinline__ void wait_vmcnt_rt(int n) {
+  switch (n) {
+#define NVFP4_WCASE(i) case i: wait_vmcnt_le<i>(); break;
+    NVFP4_WCASE(0) NVFP4_WCASE(1) NVFP4_WCASE(2) NVFP4_WCASE(3) NVFP4_WCASE(4) NVFP4_WCASE(5)
+    NVFP4_WCASE(6) NVFP4_WCASE(7) NVFP4_WCASE(8) NVFP4_WCASE(9) NVFP4_WCASE(10) NVFP4_WCASE(11)
+    NVFP4_WCASE(12) NVFP4_WCASE(13) NVFP4_WCASE(14) NVFP4_WCASE(15) NVFP4_WCASE(16)
+    NVFP4_WCASE(17) NVFP4_WCASE(18) NVFP4_WCASE(19) NVFP4_WCASE(20) NVFP4_WCASE(21)
+    NVFP4_WCASE(22)
+#undef NVFP4_WCASE
+    default: wait_vmcnt_le<23>(); break;
+  }
+}
+
 template <int FC>
-__global__ void __launch_bounds__(kFwThreads)
-moe_fc_wide(const _Float16* __restrict__ act, const int32_t* __restrict__ plists,
-            const int32_t* __restrict__ tlists, const int32_t* __restrict__ counts, int T,
-            uint32_t* __restrict__ pmax, int32_t* __restrict__ etile, int nt1,
-            const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_sf,
-            const float* __restrict__ w_g, int N, int K, int R, void* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) _Float16 xs[2][kFwTok * kFwPitch];
-  __shared__ int spair[kFwTok];   // pair of each token slot of the pass
-  __shared__ int srow[kFwTok];    // its activation row
-  __shared__ int sexp[kFwTok];    // fc2: exponent e of the pair's largest h
-  __shared__ float redmax[FC == 1 ? kFwThreads / 64 : 1][kFwTok];   // fc1: per-wave largest h
-  // fc2: factor 2^(et - e) of each fc1 row tile t of each slot's pair
-  __shared__ _Float16 sfac[FC == 2 ? kFwMaxT1 : 1][kFwTok];
-  // workgroups of one expert on one XCD (consecutive workgroup ids go to
-  // consecutive XCDs), so the expert's activations are fetched into one L2
-  int bx = blockIdx.x, e = blockIdx.y;
+__global__ void __launch_bounds__(kMfThreads, 3)
+moe_fc(const _Float16* __restrict__ act, const int32_t* __restrict__ plists,
+       const int32_t* __restrict__ tlists, const int32_t* __restrict__ counts, int T,
+       uint32_t* __restrict__ pmax, int32_t* __restrict__ etile, int nt1, int tiles,
+       const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_sf,
+       const float* __restrict__ w_g, int N, int K, void* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kMfWBufs * kMfWB + kMfABufs1 * kMfTileB];
+  __shared__ int srow[kMfTok];     // activation row of each token slot of the pass
+  __shared__ int spair[kMfTok];    // its pair
+  __shared__ int scnt;             // the expert's token count
+  __shared__ int sexp[FC == 2 ? kMfTok : 1];                    // fc2: exponent e of the pair's largest h
+  __shared__ signed char sdif[FC == 2 ? kMfMaxT1 : 1][kMfTok];  // fc2: et - e per fc1 row tile
+  __shared__ float redmax[FC == 1 ? 4 : 1][kMfTok];             // fc1: largest h per wave
+
+  // grid x = (pass, row tile), y = expert; the workgroups of one expert run
+  // on one XCD (consecutive workgroup ids go to consecutive XCDs), its passes
+  // of one row tile one XCD round apart
+  int bxz = blockIdx.x, e = blockIdx.y;
   if ((gridDim.y & 7) == 0) {
     const int L = blockIdx.x + gridDim.x * blockIdx.y;
     const int slot = L >> 3;
-    bx = slot % gridDim.x;
+    bxz = slot % gridDim.x;
     e = (slot / gridDim.x) * 8 + (L & 7);
   }
+  const int bx = bxz % tiles, z0 = bxz / tiles, zs = gridDim.x / tiles;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int32_t* pl = plists + (int64_t)e * T;
-  const int32_t* tl = tlists + (int64_t)e * T;
-  // the first pass starts at the list head: load it together with the count
-  int lp = 0, lt = 0;
-  if (blockIdx.z == 0 && tid < kFwTok) {
-    const int idx = tid < T ? tid : T - 1;
-    lp = pl[idx];
-    if (FC == 1) lt = tl[idx];
-  }
-  const int cnt = counts[e];
-  const int np = (cnt + kFwTok - 1) / kFwTok;   // passes
-  if ((int)blockIdx.z >= np) return;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool wcopy = wave < 2;                   // waves 0-1 copy weights, 2-3 activations
+  const int ct = tid & 127;                      // index among the copying threads
   const int r32 = lane & 31, h = lane >> 5;
-  const int nch = (K + kFwKC - 1) / kFwKC;
-  const int nchp = (nch + kFwWBuf - 1) / kFwWBuf * kFwWBuf;   // whole rounds of four (extra chunks are zero)
-  const int tiles = (N + kFwRows - 1) / kFwRows;
-  const int xt0 = bx * R;
-  const int ntile = (tiles - xt0 < R) ? tiles - xt0 : R;
-  const float ge = w_g[e];
+  const int nst = K / kMfKC;
+  const int n0 = bx * kMfRows;
   const uint8_t* we = w + (int64_t)e * N * (K / 2);
   const uint8_t* se = w_sf + (int64_t)e * N * (K / 16);
+  const uint32_t l0 = lds_addr(lds);
+  const uint32_t la = l0 + kMfWBufs * kMfWB;     // activation ring
+  const float ge = w_g[e];
 
-  // this lane's weight row in row tile ti (rows past N re-read row N-1;
-  // they are not stored)
-  auto wrow = [&](int ti, const uint8_t*& wr, const uint8_t*& sr) __attribute__((always_inline)) {
-    int n = (xt0 + ti) * kFwRows + wave * 32 + r32;
-    n = n < N ? n : N - 1;
-    wr = we + (int64_t)n * (K / 2);
-    sr = se + (int64_t)n * (K / 16);
-  };
-  WChunk wb[kFwWBuf];
-  // chunk c of a row (chunks past K re-read k = 0; compute() zeroes them)
-  auto load_w = [&](const uint8_t* wr, const uint8_t* sr, int c, WChunk& d) __attribute__((always_inline)) {
-    int k = c * kFwKC + 64 * h;
-    k = k < K ? k : 0;
-    d.q0 = *reinterpret_cast<const uint4*>(wr + k / 2);
-    d.q1 = *reinterpret_cast<const uint4*>(wr + k / 2 + 16);
-    d.sc = *reinterpret_cast<const uint32_t*>(sr + k / 16);
-  };
-
-  // staging: vector i of a thread = token slot kFwSlotsPerVec * i + tid /
-  // kFwRowThreads, 8 k at 8 (tid % kFwRowThreads); only the pass's token
-  // tiles are staged
-  v8h stg[kFwWBuf][kFwVec];
-  const int kq = tid % (kFwKC / 8);
-  int64_t abase[kFwVec];     // element offset of the slot's activation row
-  bool sval[kFwVec];
-  // All kFwVec loads are issued whatever the pass's token count (slots past
-  // it read a valid row and are never stored), so every step issues the same
-  // number of loads and the compiler's load-counter waits stay exact; with a
-  // count-dependent number of loads it waits conservatively, for loads issued
-  // only one step earlier.
-  auto stage_load = [&](int c, v8h (&dst)[kFwVec]) __attribute__((always_inline)) {
-    const int k0 = c * kFwKC + 8 * kq;
-    const int k = k0 < K ? k0 : 8 * kq;
+  // weight copies (waves 0-1): code copy i fills LDS piece i * 128 + ct of
+  // the stage (row (i * 128 + ct) / 2), the E4M3 copy the dword of row ct;
+  // rows past N re-read row N - 1 (their results are not stored)
+  uint32_t cofs[2], sofs;
 #pragma unroll
-    for (int i = 0; i < kFwVec; ++i) dst[i] = *reinterpret_cast<const v8h*>(act + abase[i] + k);
-  };
-  auto stage_store = [&](int c, const v8h (&src)[kFwVec], _Float16* xb, int ntt) __attribute__((always_inline)) {
-    const bool kv = c * kFwKC + 8 * kq < K;
-    const int ct = c * kFwKC / kFwRows;   // fc2: fc1 row tile of the chunk
-    const int t = ct < nt1 ? ct : nt1 - 1;
-#pragma unroll
-    for (int i = 0; i < kFwVec; ++i) {
-      if (kFwSlotsPerVec * i / 32 < ntt) {
-        v8h val = src[i];
-        if constexpr (FC == 2) {
-          const _Float16 f = sfac[t][kFwSlotsPerVec * i + tid / kFwRowThreads];
-          const v2h f2 = {f, f};
-          v2h* pv = reinterpret_cast<v2h*>(&val);
-          pv[0] = pv[0] * f2; pv[1] = pv[1] * f2; pv[2] = pv[2] * f2; pv[3] = pv[3] * f2;
-        }
-        if (!(kv && sval[i])) val = v8h{0, 0, 0, 0, 0, 0, 0, 0};
-        *reinterpret_cast<v8h*>(xb + (kFwSlotsPerVec * i + tid / kFwRowThreads) * kFwPitch + 8 * kq) = val;
-      }
-    }
+  for (int i = 0; i < 2; ++i) {
+    const int pos = i * 128 + ct, r = pos >> 1;
+    const int j = (pos & 1) ^ (((r >> 2) ^ (r >> 3)) & 1);
+    const uint32_t n = (uint32_t)(n0 + r < N ? n0 + r : N - 1);
+    cofs[i] = n * (uint32_t)(K / 2) + 16u * j;
+  }
+  sofs = (uint32_t)(n0 + ct < N ? n0 + ct : N - 1) * (uint32_t)(K / 16);
+  auto issue_w = [&](int c) __attribute__((always_inline)) {
+    const uint32_t lb = l0 + (c % kMfWBufs) * kMfWB;
+    dma16(we, cofs[0] + 32u * c, lb + 16 * (0 * 128 + 64 * wave));
+    dma16(we, cofs[1] + 32u * c, lb + 16 * (1 * 128 + 64 * wave));
+    dma4(se, sofs + 4u * c, lb + kMfCodeB + 4 * 64 * wave);
   };
 
-  v16f acc[kFwTT];
-  auto compute = [&](int c, const _Float16* xb, const WChunk& d, int ntt) __attribute__((always_inline)) {
-    const bool kv = c * kFwKC + 64 * h < K;
-    const uint32_t words[8] = {d.q0.x, d.q0.y, d.q0.z, d.q0.w, d.q1.x, d.q1.y, d.q1.z, d.q1.w};
-    _Float16 s16[4];
-    s16[0] = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)d.sc, 0);
-    s16[1] = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)d.sc, 1);
-    s16[2] = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)d.sc, 2);
-    s16[3] = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)d.sc, 3);
-    // the chunk's eight weight fragments once, then per token tile its eight
-    // activation fragments read together before its eight MFMAs (one LDS
-    // round trip per tile rather than per MFMA; each accumulator still sums
-    // its fragments in the order m = 0..7)
-    v8h af[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) af[m] = dequant8_w(kv ? words[m] : 0u, s16[m >> 1]);
-#pragma unroll
-    for (int tt = 0; tt < kFwTT; ++tt) {
-      if (tt >= ntt) break;   // wave-uniform
-      v8h bf[8];
-#pragma unroll
-      for (int m = 0; m < 8; ++m)
-        bf[m] = *reinterpret_cast<const v8h*>(xb + (32 * tt + r32) * kFwPitch + 64 * h + 8 * m);
-#pragma unroll
-      for (int m = 0; m < 8; ++m) acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[m], bf[m], acc[tt], 0, 0, 0);
-    }
-  };
+  const bool first_z = z0 == 0;
+  // the weights of the first stages depend on nothing else: in flight before
+  // the token count is known (a z > 0 workgroup is usually idle: it waits)
+  if (first_z && wcopy) {
+    for (int c = 0; c < kMfWBufs - 1 && c < nst; ++c) issue_w(c);
+  }
+  // the count, the lists and (fc2) the exponents are read by waves 2-3 only:
+  // a load of waves 0-1 would make the compiler wait for their copies
+  const int32_t* pl = plists + (int64_t)e * T;
+  const int32_t* tl = tlists + (int64_t)e * T;
+  // the first pass starts at the list head: wave 2 reads it together with
+  // the count (entries past the count are never used)
+  int hp = 0, ht = 0;
+  if (z0 == 0 && wave == 2) {
+    const int i = lane < T ? lane : T - 1;
+    hp = pl[i];
+    if (FC == 1) ht = tl[i];
+  }
+  if (tid == 128) scnt = counts[e];
+  lds_barrier();
+  const int cnt = scnt;
+  const int np = (cnt + kMfTok - 1) / kMfTok;   // passes
+  if (z0 >= np) {
+    wait_vmcnt_le<0>();   // no copy into LDS outlives the workgroup
+    return;
+  }
+  // operand read offsets (bytes within a stage buffer)
+  const int r = 32 * wave + r32;
+  const uint32_t ca = 16u * (2 * r + (h ^ (((r >> 2) ^ (r >> 3)) & 1)));   // code piece h of row r
+  const uint32_t sa = kMfCodeB + 4u * r;                                    // E4M3 dword of row r
+  const int rot = (r32 + ((r32 >> 3) & 3)) & 7;  // rotation of slots r32 and 32 + r32
+  const int b4 = (4 * h + rot) & 7;              // position of the lane's first piece
+  const uint32_t ab0 = 128u * r32 + 16u * b4;    // slot r32 of tile 0, piece 4h
+  typedef const __attribute__((address_space(3))) unsigned char* lptr;
 
-  // results of row tile ti: acc[tt][r] = weight row n0 + 8 (r / 4) + 4 h +
-  // r % 4, token slot 32 tt + r32
-  auto epilogue = [&](int ti, int ntok, int ntt) __attribute__((always_inline)) {
-    const int xt = xt0 + ti;
-    const int n0 = xt * kFwRows + wave * 32;
-    if constexpr (FC == 1) {
-#pragma unroll
-      for (int tt = 0; tt < kFwTT; ++tt) {
-        if (tt >= ntt) break;
-        float m = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) m = __builtin_fmaxf(m, relu2_f32(acc[tt][r] * ge));
-        if (n0 >= N) m = 0.0f;
-        m = __builtin_fmaxf(m, __shfl_xor(m, 32, 64));
-        if (h == 0) redmax[wave][32 * tt + r32] = m;
-      }
-      lds_barrier();
-#pragma unroll
-      for (int tt = 0; tt < kFwTT; ++tt) {
-        if (tt >= ntt) break;
-        const int slot = 32 * tt + r32;
-        float tmax = redmax[0][slot];
-#pragma unroll
-        for (int wv = 1; wv < kFwThreads / 64; ++wv) tmax = __builtin_fmaxf(tmax, redmax[wv][slot]);
-        const int ex = exponent_of(__float_as_uint(tmax));
-        const float sc = __builtin_ldexpf(1.0f, -ex);
-        const bool sv = slot < ntok;
-        const int p = spair[slot];
-        if (sv && n0 < N) {
-          _Float16* hp = reinterpret_cast<_Float16*>(out) + (int64_t)p * N + n0 + 4 * h;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            v4h o4;
-            o4[0] = (_Float16)(relu2_f32(acc[tt][4 * q + 0] * ge) * sc);
-            o4[1] = (_Float16)(relu2_f32(acc[tt][4 * q + 1] * ge) * sc);
-            o4[2] = (_Float16)(relu2_f32(acc[tt][4 * q + 2] * ge) * sc);
-            o4[3] = (_Float16)(relu2_f32(acc[tt][4 * q + 3] * ge) * sc);
-            *reinterpret_cast<v4h*>(hp + 8 * q) = o4;
-          }
-        }
-        if (sv && wave == 0 && h == 0) {
-          etile[(int64_t)p * nt1 + xt] = ex;
-          atomicMax(pmax + p, __float_as_uint(tmax));
-        }
-      }
-    } else {
-#pragma unroll
-      for (int tt = 0; tt < kFwTT; ++tt) {
-        if (tt >= ntt) break;
-        const int slot = 32 * tt + r32;
-        const float scale = __builtin_ldexpf(ge, sexp[slot]);
-        if (slot < ntok && n0 < N) {
-          float* op = reinterpret_cast<float*>(out) + (int64_t)spair[slot] * N + n0 + 4 * h;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float4 v;
-            v.x = acc[tt][4 * q + 0] * scale;
-            v.y = acc[tt][4 * q + 1] * scale;
-            v.z = acc[tt][4 * q + 2] * scale;
-            v.w = acc[tt][4 * q + 3] * scale;
-            *reinterpret_cast<float4*>(op + 8 * q) = v;
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int tt = 0; tt < kFwTT; ++tt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[tt][r] = 0.0f;
-  };
-
-#pragma unroll
-  for (int tt = 0; tt < kFwTT; ++tt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[tt][r] = 0.0f;
-  for (int z = blockIdx.z; z < np; z += gridDim.z) {
+  for (int z = z0; z < np; z += zs) {
+    const bool wpre = first_z && z == z0;   // the first weight stages are issued
     // balanced passes: the first cnt % np passes take one token more
     const int base = cnt / np, rem = cnt % np;
     const int ntok = base + (z < rem ? 1 : 0);
     const int t0 = z * base + (z < rem ? z : rem);
-    const int ntt = (ntok + 31) / 32;
-    if (z != (int)blockIdx.z) __syncthreads();   // a previous pass is done with the LDS buffers
-    if (t0 != 0 && tid < kFwTok) {
-      lp = pl[t0 + (tid < ntok ? tid : 0)];
-      if (FC == 1) lt = tl[t0 + (tid < ntok ? tid : 0)];
+    const int ntt = (ntok + 31) / 32;                    // token tiles of the pass
+    if (z != z0) lds_barrier();   // the previous pass is done with the LDS
+    // slots past the pass take the pass's first token (computed, never stored)
+    if (wave == 2) {
+      int p, t;
+      if (z == 0) {
+        const int p0 = __shfl(hp, 0, 64), t0h = __shfl(ht, 0, 64);
+        p = lane < ntok ? hp : p0;
+        t = lane < ntok ? ht : t0h;
+      } else {
+        const int idx = t0 + (lane < ntok ? lane : 0);
+        p = pl[idx];
+        t = FC == 1 ? tl[idx] : 0;
+      }
+      spair[lane] = p;
+      srow[lane] = FC == 1 ? t : p;
     }
-    // slots past the pass use token 0 / pair 0 (computed, never stored)
-    if (tid < kFwTok) {
-      const int p = tid < ntok ? lp : 0;
-      spair[tid] = p;
-      srow[tid] = FC == 1 ? (tid < ntok ? lt : 0) : p;
-    }
-    // weights of chunks 0..2, then (fc2) the pairs' maxima and the
-    // activations of chunks 0 and 1, all in flight together
-    const uint8_t *wr, *sr;
-    wrow(0, wr, sr);
-    load_w(wr, sr, 0, wb[0]);
-    load_w(wr, sr, 1, wb[1]);
-    load_w(wr, sr, 2, wb[2]);
     lds_barrier();
-#pragma unroll
-    for (int i = 0; i < kFwVec; ++i) {
-      const int slot = kFwSlotsPerVec * i + tid / kFwRowThreads;
-      sval[i] = slot < ntok;
-      abase[i] = (int64_t)srow[slot] * K;
-    }
-    stage_load(0, stg[0]);
-    stage_load(1, stg[1]);
-    stage_load(2, stg[2]);
     if constexpr (FC == 2) {
-      // each slot's exponent e and the factors of its fc1 row tiles
-      // (d = et - e <= 0; d > 0 only for an all-zero tile; factors below
-      // FP16's range are 0)
-      for (int idx = tid; idx < kFwTok * nt1; idx += kFwThreads) {
-        const int t = idx / kFwTok, slot = idx - t * kFwTok;
-        const int p = spair[slot];
-        const int ex = exponent_of(pmax[p]);
-        int d = etile[(int64_t)p * nt1 + t] - ex;
-        d = d > 0 ? 0 : d;
-        sfac[t][slot] = d < -24 ? (_Float16)0.0f : (_Float16)__builtin_ldexpf(1.0f, d);
-        if (t == 0) sexp[slot] = ex;
+      // each slot's exponent e and, per fc1 row tile, et - e (> 0 only for an
+      // all-zero tile, whose products are zero: clamped to 0)
+      if (!wcopy) {
+        for (int idx = ct; idx < kMfTok * nt1; idx += 128) {
+          const int t = idx / kMfTok, slot = idx - t * kMfTok;
+          const int p = spair[slot];
+          const int ex = exponent_of(pmax[p]);
+          int d = etile[(int64_t)p * nt1 + t] - ex;
+          d = d > 0 ? 0 : (d < -126 ? -126 : d);
+          sdif[t][slot] = (signed char)d;
+          if (t == 0) sexp[slot] = ex;
+        }
+      }
+    }
+    // everything below is instantiated for one and for two token tiles, so
+    // the accumulators stay in the same registers through the stage loop
+    auto run = [&](auto nc) __attribute__((always_inline)) {
+    constexpr int NTT = nc;
+    constexpr int abufs = NTT == 1 ? kMfABufs1 : kMfABufs2;
+    constexpr uint32_t abuf = NTT * kMfTileB;
+    // activation copies (waves 2-3): copy i fills LDS piece i * 128 + ct of
+    // the stage (slot (i * 128 + ct) / 8; the slot's piece (ct - rot) mod 8)
+    const _Float16* aptr[2 * kMfMaxT];
+#pragma unroll
+    for (int i = 0; i < 2 * kMfMaxT; ++i) {
+      const int pos = i * 128 + ct, s = pos >> 3;
+      const int j = ((pos & 7) - (s + ((s >> 3) & 3))) & 7;
+      aptr[i] = act + (int64_t)srow[s < kMfTok ? s : 0] * K + 8 * j;
+    }
+    auto issue_a = [&](int c) __attribute__((always_inline)) {
+      const uint32_t lb = la + (c % abufs) * abuf;
+#pragma unroll
+      for (int i = 0; i < 2 * kMfMaxT; ++i)
+        if (i < 2 * NTT) dma16_at(aptr[i] + kMfKC * c, lb + 16 * (i * 128 + 64 * (wave - 2)));
+    };
+    if (wcopy) {
+      if (!wpre)
+        for (int c = 0; c < kMfWBufs - 1 && c < nst; ++c) issue_w(c);
+    } else {
+      for (int c = 0; c < abufs - 1 && c < nst; ++c) issue_a(c);
+    }
+    if constexpr (FC == 2) lds_barrier();   // sexp / sdif written
+
+    v16f acc[kMfMaxT];
+#pragma unroll
+    for (int i = 0; i < kMfMaxT; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][q] = 0.0f;
+    _Float16 fac[kMfMaxT];   // fc2: factors of the current 128-k range
+
+    auto compute = [&](uint32_t st, uint32_t sta, auto nwc) __attribute__((always_inline)) {
+      constexpr int NW = nwc;
+      // per-stage bases kept opaque, so every operand read below is a base
+      // plus an immediate; all of the stage's reads are issued before the
+      // first dequantization (the scheduling barrier keeps them there)
+      uint32_t bw = st, b0 = sta + ab0, b1 = b0 - 128u;
+      asm volatile("" : "+v"(bw), "+v"(b0), "+v"(b1));
+      const lptr pw = (lptr)(uintptr_t)bw;
+      const u32x4 cw = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(pw + ca);
+      const uint32_t sw = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(pw + sa);
+      v8h bf[4][NW];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const lptr pa = (lptr)(uintptr_t)(m < 8 - b4 ? b0 : b1);
+#pragma unroll
+        for (int i = 0; i < NW; ++i)
+          bf[m][i] = *reinterpret_cast<const __attribute__((address_space(3))) v8h*>(pa + 16 * m + 32 * 128 * i);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // this lane's two 16-blocks: bytes 2h and 2h + 1 of the row's dword
+      const uint32_t sh = sw >> (16 * h);
+      const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)sh, 0);
+      const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)sh, 1);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const v8h a = dequant8_w(cw[m], m < 2 ? s0 : s1);
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+          v8h b = bf[m][i];
+          if constexpr (FC == 2) {
+            const v2h f2 = {fac[i], fac[i]};
+            v2h* pb = reinterpret_cast<v2h*>(&b);
+            pb[0] = pb[0] * f2; pb[1] = pb[1] * f2; pb[2] = pb[2] * f2; pb[3] = pb[3] * f2;
+          }
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[i], 0, 0, 0);
+        }
+      }
+    };
+
+    for (int c = 0; c < nst; ++c) {
+      // this wave's copies of stage c landed: at most those of the stages
+      // issued after it remain
+      if (wcopy) {
+        const int k = (nst - 1 - c) < kMfWBufs - 2 ? nst - 1 - c : kMfWBufs - 2;
+        wait_vmcnt_rt(k * kMfWOps);
+      } else {
+        const int k = (nst - 1 - c) < abufs - 2 ? nst - 1 - c : abufs - 2;
+        wait_vmcnt_rt(k * 2 * NTT);
+      }
+      lds_barrier();   // every copy of stage c landed; stage c - 1 is no longer read
+      if (wcopy) {
+        if (c + kMfWBufs - 1 < nst) issue_w(c + kMfWBufs - 1);
+      } else {
+        if (c + abufs - 1 < nst) issue_a(c + abufs - 1);
+      }
+      if constexpr (FC == 2) {
+        if ((c & 1) == 0) {   // a new 128-k range: fc1 row tile c / 2
+#pragma unroll
+          for (int i = 0; i < kMfMaxT; ++i) {
+            const int d = sdif[c >> 1][32 * i + r32];
+            fac[i] = d < -24 ? (_Float16)0.0f : (_Float16)__builtin_ldexpf(1.0f, d);
+          }
+        }
+      }
+      const uint32_t st = l0 + (c % kMfWBufs) * kMfWB, sta = la + (c % abufs) * abuf;
+      compute(st, sta, nc);
+    }
+
+    // results: acc[i][q] = weight row n0 + 32 wave + 8 (q / 4) + 4 h + q % 4,
+    // token slot 32 i + r32
+    const bool rv = n0 + 32 * wave < N;   // N % 64 == 0: a wave's 32 rows are all in or all out
+    if constexpr (FC == 1) {
+#pragma unroll
+      for (int i = 0; i < kMfMaxT; ++i) {
+        if (i < ntt) {
+          float mx = 0.0f;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) mx = __builtin_fmaxf(mx, relu2_f32(acc[i][q] * ge));
+          if (!rv) mx = 0.0f;
+          mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
+          if (h == 0) redmax[wave][32 * i + r32] = mx;
+        }
       }
       lds_barrier();
-    }
-    stage_store(0, stg[0], xs[0], ntt);
-    lds_barrier();
-    // chunk c of a tile uses weight and staging register buffers c % 4 and
-    // LDS buffer c % 2 (nchp is a multiple of four, so this holds across
-    // tiles).  Step c loads the activations and the weights of chunk c + 3,
-    // past the tile's end those of the next tile (of this one past the last:
-    // re-read, unused), so both have two steps of other work before use.
-    for (int ti = 0; ti < ntile; ++ti) {
-      const uint8_t *wn, *sn;
-      wrow(ti + 1 < ntile ? ti + 1 : ti, wn, sn);
-      auto step = [&](int c, auto jc) __attribute__((always_inline)) {
-        constexpr int j = decltype(jc)::value;
-        stage_load(c + 3 < nchp ? c + 3 : c + 3 - nchp, stg[(j + 3) % kFwWBuf]);
-        const bool nx = c + 3 >= nchp;
-        load_w(nx ? wn : wr, nx ? sn : sr, nx ? c + 3 - nchp : c + 3, wb[(j + 3) % kFwWBuf]);
-        compute(c, xs[j & 1], wb[j], ntt);
-        stage_store(c + 1 < nchp ? c + 1 : 0, stg[(j + 1) % kFwWBuf], xs[(j + 1) & 1], ntt);
-        lds_barrier();
-      };
-      for (int c = 0; c < nchp; c += kFwWBuf) {
-        step(c, IntC<0>{});
-        step(c + 1, IntC<1>{});
-        step(c + 2, IntC<2>{});
-        step(c + 3, IntC<3>{});
+#pragma unroll
+      for (int i = 0; i < kMfMaxT; ++i) {
+        const int slot = 32 * i + r32;
+        if (i < ntt && slot < ntok) {
+          const float tmax = __builtin_fmaxf(__builtin_fmaxf(redmax[0][slot], redmax[1][slot]),
+                                             __builtin_fmaxf(redmax[2][slot], redmax[3][slot]));
+          const int ex = exponent_of(__float_as_uint(tmax));
+          const float sc = __builtin_ldexpf(1.0f, -ex);
+          const int p = spair[slot];
+          if (rv) {
+            _Float16* hp = reinterpret_cast<_Float16*>(out) + (int64_t)p * N + n0 + 32 * wave + 4 * h;
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+              v4h o4;
+              o4[0] = (_Float16)(relu2_f32(acc[i][4 * qd + 0] * ge) * sc);
+              o4[1] = (_Float16)(relu2_f32(acc[i][4 * qd + 1] * ge) * sc);
+              o4[2] = (_Float16)(relu2_f32(acc[i][4 * qd + 2] * ge) * sc);
+              o4[3] = (_Float16)(relu2_f32(acc[i][4 * qd + 3] * ge) * sc);
+              *reinterpret_cast<v4h*>(hp + 8 * qd) = o4;
+            }
+          }
+          if (wave == 0 && h == 0) {
+            etile[(int64_t)p * nt1 + bx] = ex;
+            atomicMax(pmax + p, __float_as_uint(tmax));
+          }
+        }
       }
-      epilogue(ti, ntok, ntt);
-      wr = wn;
-      sr = sn;
+    } else {
+#pragma unroll
+      for (int i = 0; i < kMfMaxT; ++i) {
+        const int slot = 32 * i + r32;
+        if (i < ntt && slot < ntok && rv) {
+          const float scale = __builtin_ldexpf(ge, sexp[slot]);
+          float* op = reinterpret_cast<float*>(out) + (int64_t)spair[slot] * N + n0 + 32 * wave + 4 * h;
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            float4 v;
+            v.x = acc[i][4 * qd + 0] * scale;
+            v.y = acc[i][4 * qd + 1] * scale;
+            v.z = acc[i][4 * qd + 2] * scale;
+            v.w = acc[i][4 * qd + 3] * scale;
+            *reinterpret_cast<float4*>(op + 8 * qd) = v;
+          }
+        }
+      }
     }
+    };
+    if (ntt == 2) run(std::integral_constant<int, 2>{});
+    else run(std::integral_constant<int, 1>{});
   }
 }
 
@@ -657,18 +701,6 @@ size_t moe_workspace_bytes(int tokens, int experts, int top_k, int hidden, int i
   const size_t ET = (size_t)experts * tokens;
   return 3 * align256(P * 4) + align256((size_t)experts * 4) + 2 * align256(ET * 4) +
          align256(P * fc1_tiles(inter) * 4) + align256(P * inter * 2) + align256(P * hidden * 4);
-}
-
-// Row tiles per workgroup.  One while the (expert, row tile) units number
-// less than four per workgroup slot: smaller units finish the layer in fewer
-// unit-lengths (for the 64-expert, 2048-row fc2 layer, 512 units of one tile
-// beat 256 of two by ~3 us); beyond that, R tiles streamed back to back share
-// one prologue.
-static int tiles_per_wg(int experts, int n, int num_cus) {
-  const int units = experts * ((n + kFwRows - 1) / kFwRows);
-  const int slots = num_cus * kFwPerCU;
-  int r = slots > 0 ? units / (2 * slots) : 1;
-  return r < 1 ? 1 : (r > 8 ? 8 : r);
 }
 
 // Device address of `scratch` on the current device, looked up once per
@@ -702,17 +734,18 @@ hipError_t launch_moe(const MoeArgs& m, hipStream_t s) {
                      ws.ids, ws.wts, ws.pmax, m.ids_out, m.w_out);
   hipLaunchKernelGGL(moe_lists, dim3(m.experts), dim3(kListThreads), 0, s, ws.ids, P, m.tokens,
                      m.top_k, ws.plists, ws.tlists, ws.counts);
-  const int zs = (m.tokens + kFwTok - 1) / kFwTok < kFwMaxZ ? (m.tokens + kFwTok - 1) / kFwTok : kFwMaxZ;
-  const int r1 = tiles_per_wg(m.experts, m.inter, m.num_cus);
-  const int r2 = tiles_per_wg(m.experts, m.hidden, m.num_cus);
-  hipLaunchKernelGGL(moe_fc_wide<1>, dim3((nt1 + r1 - 1) / r1, m.experts, zs), dim3(kFwThreads), 0, s,
-                     reinterpret_cast<const _Float16*>(m.x), ws.plists, ws.tlists, ws.counts,
-                     m.tokens, ws.pmax, ws.etile, nt1, m.w1, m.w1_sf, m.w1_g, m.inter, m.hidden, r1,
+  // fc1 and fc2: 128-row tiles x passes of up to 64 tokens; grid x = (pass,
+  // row tile), y = expert
+  const int zt = (m.tokens + kMfTok - 1) / kMfTok;
+  const int zs = zt < kMfMaxZ ? zt : kMfMaxZ;
+  const int t1 = (m.inter + kMfRows - 1) / kMfRows, t2 = (m.hidden + kMfRows - 1) / kMfRows;
+  hipLaunchKernelGGL(moe_fc<1>, dim3(t1 * zs, m.experts), dim3(kMfThreads), 0, s,
+                     reinterpret_cast<const _Float16*>(m.x), ws.plists, ws.tlists, ws.counts, m.tokens,
+                     ws.pmax, ws.etile, nt1, t1, m.w1, m.w1_sf, m.w1_g, m.inter, m.hidden,
                      reinterpret_cast<void*>(ws.h));
-  const int t2 = (m.hidden + kFwRows - 1) / kFwRows;
-  hipLaunchKernelGGL(moe_fc_wide<2>, dim3((t2 + r2 - 1) / r2, m.experts, zs), dim3(kFwThreads), 0, s,
-                     ws.h, ws.plists, ws.tlists, ws.counts, m.tokens, ws.pmax, ws.etile, nt1, m.w2,
-                     m.w2_sf, m.w2_g, m.hidden, m.inter, r2, reinterpret_cast<void*>(ws.o));
+  hipLaunchKernelGGL(moe_fc<2>, dim3(t2 * zs, m.experts), dim3(kMfThreads), 0, s, ws.h, ws.plists,
+                     ws.tlists, ws.counts, m.tokens, ws.pmax, ws.etile, nt1, t2, m.w2, m.w2_sf, m.w2_g,
+                     m.hidden, m.inter, reinterpret_cast<void*>(ws.o));
   hipLaunchKernelGGL(moe_combine4, dim3(m.tokens, (m.hidden + 1023) / 1024), dim3(256), 0, s, ws.o,
                      ws.wts, m.top_k, m.hidden, reinterpret_cast<_Float16*>(m.out));
   return hipGetLastError();
