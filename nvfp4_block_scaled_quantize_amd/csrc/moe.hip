@@ -109,7 +109,7 @@ moe_route(const float* __restrict__ logits, const float* __restrict__ bias, int 
   __shared__ int sel_e[4][16];      // chosen experts by rank
   __shared__ float sel_s[4][16];    // their unbiased scores
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int t_raw = blockIdx.x * 4 + wv;
+  const int t_raw = blockIdx.x * (blockDim.x >> 6) + wv;
   const bool tv = t_raw < T;             // waves past the last token idle but reach the barriers
   const int t = tv ? t_raw : 0;
   const float ninf = -__builtin_inff();
@@ -729,7 +729,9 @@ hipError_t launch_moe(const MoeArgs& m, hipStream_t s) {
   const int P = m.tokens * m.top_k;
   MoeWs ws = carve(m.workspace, m.tokens, m.experts, P, m.hidden, m.inter);
   const int nt1 = fc1_tiles(m.inter);
-  hipLaunchKernelGGL(moe_route, dim3((m.tokens + 3) / 4), dim3(256), 0, s, m.logits, m.bias,
+  // one wave (one token) per workgroup: the selection steps synchronize a
+  // single wave, not the slowest of several
+  hipLaunchKernelGGL(moe_route, dim3(m.tokens), dim3(64), 0, s, m.logits, m.bias,
                      m.tokens, m.experts, m.top_k, m.n_group, m.topk_group, m.norm, m.scaling,
                      ws.ids, ws.wts, ws.pmax, m.ids_out, m.w_out);
   hipLaunchKernelGGL(moe_lists, dim3(m.experts), dim3(kListThreads), 0, s, ws.ids, P, m.tokens,
