@@ -49,8 +49,8 @@ namespace {
 
 constexpr int kMaxThreads = 256;     // per-row kernel and fallback
 constexpr int kMaxUnits = 16;        // 8-value units per thread held in registers
-constexpr int kTabUnits = 4;         // persistent SwiGLU kernel: units per thread,
-constexpr int kTabThreads = 512;     // at most this many threads per workgroup
+constexpr int kTabUnits = 2;         // persistent SwiGLU kernel: units per thread,
+constexpr int kTabThreads = 1024;    // at most this many threads per workgroup
 constexpr uint32_t kTabE0 = 103;     // smallest tabulated biased exponent: |g| >= 2^-24
 constexpr int kTabHalf = 32 * 128;   // entries per sign: exponents 103..134 (|g| < 256)
 constexpr int kTabMinRows = 1024;    // below this the per-workgroup table does not pay off
