@@ -12,24 +12,19 @@
 //                  order.
 //  2. lists      : one workgroup per expert writes the pairs (token, rank)
 //                  routed to it, in pair order, and their count.
-//  3. fc1        : grid (inter/256 row tiles, experts, token passes), 8 waves
-//                  = 4 groups of 64 weight rows x 2 token halves,
-//                  v_mfma_f32_32x32x16_f16.  Per 128-k stage the tile's FP4
-//                  codes and E4M3 bytes and the expert's FP16 token rows are
-//                  copied global -> LDS by global_load_lds, two stages ahead;
-//                  weights are dequantized in registers (exact in FP16).
-//                  Passes hold up to 128 tokens (an expert with more spreads
-//                  over several workgroups).  h = relu(x . W1^T * g1)^2 is
-//                  stored as FP16 scaled by 2^-et per (pair, 256-row tile),
-//                  et the exponent of the tile's largest h; the pair's
-//                  overall largest h is an integer max of fp32 bits (order
-//                  independent).
-//  4. fc2        : grid (hidden/512 row tiles, experts, token passes of up to
-//                  64), 8 waves of 64 rows.  Same structure on h; the products
-//                  of each 256-k range (one fc1 tile) are accumulated apart and
-//                  folded into the total with the factor 2^(et - e), e =
-//                  exponent of the pair's largest h; o = total * g2 * 2^e in
-//                  fp32 per pair.
+//  3. fc1        : units of (expert, 128 weight rows, pass of up to 64 of
+//                  the expert's tokens), four waves each,
+//                  v_mfma_f32_32x32x16_f16 with weights dequantized in
+//                  registers (exact in FP16); operands copied global -> LDS
+//                  by global_load_lds, several 64-k stages ahead.
+//                  h = relu(x . W1^T * g1)^2 is stored as FP16 scaled by
+//                  2^-et per (pair, 128-row tile), et the exponent of the
+//                  tile's largest h; the pair's overall largest h is an
+//                  integer max of fp32 bits (order independent).
+//  4. fc2        : the same units on h.  The activations of each 128-k
+//                  range (one fc1 tile) are multiplied by 2^(et - e) in FP16,
+//                  e = exponent of the pair's largest h; o = acc * g2 * 2^e
+//                  in fp32 per pair.
 //  5. combine    : out[t] = sum_j w[t,j] * o[t*top_k + j] in rank order, FP16.
 #include "device_common.h"
 #include "internal.h"
@@ -302,8 +297,8 @@ __device__ __forceinline__ v8h dequant8_w(uint32_t codes, _Float16 s16) {
 
 // Expert FFN layers (fc1, fc2).  A unit of work is (expert e, tile of 128
 // weight rows, pass of up to 64 of the expert's tokens); an expert with more
-// tokens is cut into balanced passes.  Workgroups are small (four waves, at
-// most 80 KiB of LDS), so two run on each compute unit and the hardware
+// tokens is cut into balanced passes.  Workgroups are small (four waves,
+// about 52 KiB of LDS), so three run on each compute unit and the hardware
 // dispatcher spreads the many short units evenly; the units of one expert
 // are dispatched next to each other on one XCD (its activations, and for
 // several passes its weight rows, are then read from that XCD's L2).
@@ -313,10 +308,10 @@ __device__ __forceinline__ v8h dequant8_w(uint32_t codes, _Float16 s16) {
 //
 // K goes in 64-k stages copied global -> LDS by global_load_lds into two
 // rings: waves 0-1 copy the weights (FP4 codes 32 B and E4M3 bytes 4 B per
-// row and stage) through an 8-stage ring whose first seven stages are
-// issued before the token count is read; waves 2-3 gather the FP16 token
-// rows (128 B per token and stage; 64-bit addresses) through an 8-stage ring
-// for one token tile, 4 for two.  Each wave's copies are the same for every
+// row and stage) through a 5-stage ring whose first four stages are issued
+// before the token count is read; waves 2-3 gather the FP16 token rows
+// (128 B per token and stage; 64-bit addresses) through a 6-stage ring for
+// one token tile, 3 for two.  Each wave's copies are the same for every
 // stage, so its vector-memory counter waits are exact; one barrier per stage
 // publishes both.  LDS layouts (16 consecutive lanes of an operand read hit
 // 16 distinct bank groups, and 8 lanes 8):
