@@ -2,27 +2,35 @@
 // FP16 output, the operation of "Fused Nvfp4 GEMM All Reduce Plugin"
 // (baked-weight inputs 0..4, output 0), for gfx950.
 //
-// Why FP16 MFMA: gfx950's scaled f8f6f4 MFMA applies power-of-two (E8M0)
-// scales per 32 K-elements, while NVFP4 carries an E4M3 scale per 16 elements
-// and the activation side an arbitrary FP32 scale per 16 elements.  The
-// dequantized weight e2m1 * e4m3 has at most 6 significant bits and lies in
-// [2^-10, 2688], so it is EXACT in FP16; the global weight scale moves to the
-// epilogue.  The activation q * c is rounded once to FP16 after a power-of-two
-// normalization (per row for the prefill kernels, per row and half round of
-// 256 k in the decode kernel) so that no value can overflow FP16; the power of
-// two returns in FP32 after the MFMAs.  Products accumulate in FP32.
+// Why FP16 MFMA for the prefill kernels: gfx950's scaled f8f6f4 MFMA applies
+// power-of-two (E8M0) scales per 32 K-elements, while NVFP4 carries an E4M3
+// scale per 16 elements and the activation side an arbitrary FP32 scale per
+// 16 elements.  The dequantized weight e2m1 * e4m3 has at most 6 significant
+// bits and lies in [2^-10, 2688], so it is EXACT in FP16; the global weight
+// scale moves to the epilogue.  The activation q * c is rounded once to FP16
+// after a power-of-two normalization (per row for the prefill kernels, per
+// row and half round of 256 k in the FP16 decode kernel) so that no value can
+// overflow FP16; the power of two returns in FP32 after the MFMAs.  Products
+// accumulate in FP32.
 //
-// Two kernel families, chosen by the batch size:
-//  * gemm_skinny (B <= 16, decode): a streaming GEMV-like pass over the weight
-//    matrix, one workgroup per 32 weight rows, each wave one interleaved
-//    eighth of K; every lane issues 16-byte loads of 32 consecutive FP4 codes
-//    of its row, converts them with v_cvt_scalef32_pk_f16_fp4 and one packed
-//    FP16 multiply by the E4M3 scale, and feeds v_mfma_f32_16x16x32_f16 with
-//    the (up to 16) activation rows as the other operand.  Each wave loads
-//    and stages the activations of its own K slice through a private LDS
-//    region, in order with its weights, so no workgroup barrier precedes the
-//    MFMAs; the eight K slices are summed in LDS in a fixed order
-//    (deterministic).
+// Three kernel families, chosen by the batch size:
+//  * gemm_skinny4 (B <= 4, decode): the raw FP4 codes of both operands on the
+//    FP4 matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4, E8M0 scales 1).
+//    The activation operand is block-diagonal -- each operand row is one
+//    (token, 16-k block) pair -- so each output is one block's unscaled dot
+//    product (exact in FP32), scaled in FP32 by the weight's E4M3 byte and the
+//    token's combined scale.  One workgroup per 32 weight rows, each wave one
+//    interleaved eighth of K, 16-byte weight loads straight into the MFMA
+//    operand; nothing is dequantized.
+//  * gemm_skinny16 (4 < B <= 16, decode): the same work split; every lane
+//    converts its 32 FP4 weight codes with v_cvt_scalef32_pk_f16_fp4 and one
+//    packed FP16 multiply by the E4M3 scale and feeds v_mfma_f32_16x16x32_f16
+//    with the (up to 16) activation rows as the other operand, so the
+//    arithmetic per weight does not grow with B.
+//    Both decode kernels load and stage the activations of each wave's own K
+//    slice through a private LDS region, in order with its weights, so no
+//    workgroup barrier precedes the MFMAs; the eight K slices are summed in
+//    LDS in a fixed order (deterministic).
 //  * gemm_wide (larger B, prefill, 16-byte weight rows, K % 64 == 0, or the
 //    pre-tiled layout): a prologue kernel writes the normalized FP16
 //    activations once; the main kernel computes 128 x 512 output tiles with 8
@@ -148,21 +156,346 @@ constexpr int kSkThreads = 512;   // 8 waves
 constexpr int kSkWaves = kSkThreads / 64;
 constexpr int kSkRows = 32;       // weight rows per workgroup: two 16-row MFMA groups
 constexpr int kSkPF = 4;          // 128-k chunks per round (all loads of a round in flight)
-constexpr int kSkHalves = 2;      // per half round: one activation load group and one 2^e per row
-constexpr int kSkHC = kSkPF / kSkHalves;
+constexpr int kSkHalves = 2;      // activation load groups per round (one 2^e per row each in
+                                  // the FP16 kernel)
+constexpr int kSkHC = kSkPF / kSkHalves;        // chunks per half round
+constexpr int kScaleOne = 0x7F7F7F7F;          // E8M0 1.0 in every byte: the MFMA's own scales unused
+
+// Per-wave LDS of the skinny kernel for NP token pairs: a half round's
+// activation operand rows (kSkHC chunks x NP pairs x 16 rows x 16 B: the
+// row's block in its half of the 32 k, zeros in the other half), as many zero
+// bytes (read by the lanes whose 32 k do not hold their row's block), the
+// half round's activation scales (kSkHC x NP x 4 lane groups x 16 B) and a
+// 16-byte slot that takes the writes of items past the last token.  The
+// K-slice reduction reuses the space after a barrier.
+constexpr int sk_aop_bytes(int np) { return kSkHC * np * 16 * 16; }
+constexpr int sk_wave_bytes(int np) { return 2 * sk_aop_bytes(np) + kSkHC * np * 64 + 16; }
+constexpr size_t skinny4_lds_bytes(int np) { return (size_t)kSkWaves * sk_wave_bytes(np); }
+constexpr size_t skinny4_red_bytes(int np) { return (size_t)kSkWaves * kSkRows * 2 * np * 4; }
+static_assert(skinny4_lds_bytes(1) >= skinny4_red_bytes(1) && skinny4_lds_bytes(2) >= skinny4_red_bytes(2),
+              "the reduction fits the stages");
+
+// Sum of a value over the four 16-lane rows of a wave, the same in every lane
+// and added in the same order: v_permlane16_swap pairs rows (0, 1) and (2, 3),
+// v_permlane32_swap the two halves.
+__device__ __forceinline__ float fold_lane_groups(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+// The FP4 operand of a scaled MFMA: 32 codes in the low four registers.
+typedef int v8i __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ v8i fp4_op(u32x4 v) {
+  return v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+}
+
+// Decode: one workgroup = 32 weight rows x all of K on the FP4 matrix cores
+// (v_mfma_scale_f32_16x16x128_f8f6f4, both operands E2M1, the instruction's
+// E8M0 scales fixed at 1).  The hardware sums over all 128 k of an
+// instruction, while every 16 k carry their own scales on both sides, so the
+// activation operand is block-diagonal: operand row m = 4 G + u stands for
+// token 2 p + u / 2 and 16-k block 2 G + u % 2 of the chunk and holds that
+// block's codes, zeros elsewhere.  Output (m, n) of one instruction is then
+// the unscaled dot product of block (2 G + u % 2) of that token and weight row
+// n: a sum of 16 E2M1 x E2M1 products, a multiple of 1/4 below 2^10, exact in
+// FP32 whatever the summation order.  The lane holding rows 4 G .. 4 G + 3 of
+// column n multiplies each by its weight's E4M3 scale times the token's FP32
+// combined scale (one rounding each) and adds it to an FP32 total per (row,
+// token).  No dequantization, no FP16 rounding, no normalization.
+// The weight operand is 16 raw code bytes per lane (lane r + 16 g: row r,
+// k = 32 g .. 32 g + 31 of the chunk), exactly as stored; the activation
+// operand uses the same (lane group, byte) positions for the same k.
+//
+// Wave w owns the interleaved 128-k chunks w, w + 8, ... in rounds of kSkPF
+// chunks.  A round issues its loads half round by half round -- the half's
+// activation items (16 B of codes = 32 k of one token; 16 B of combined
+// scales = 4 blocks of one token), then the half's weight codes and E4M3
+// bytes -- so with the in-order load counter each half's activations arrive
+// before its weights and the first half is processed while the second
+// streams in.  The activation items are written into the wave's own LDS
+// region at their operand positions (the zero positions are written once at
+// the start) and read back one 16-byte operand per lane and pair: LDS
+// operations of one wave run in order, so no barrier.  At the end the four
+// lane groups' totals are folded in registers (cross-row lane swaps) and the
+// eight K slices summed in LDS, both in a fixed order (deterministic).
+// Rounds that lie inside K and the wave's range run without validity selects;
+// the last partial round clamps its addresses and zeroes codes and scales
+// outside (scales too, so that no NaN from an unused byte can enter).
+// AV: activation codes and scales 16-byte aligned with K % 64 == 0 (16-byte
+// loads), else byte and dword loads.  NP: token pairs (B <= 2 NP).
+// WL: weight layout (kWPlain, kWTiled = pre-tiled, each wave-load of 16 rows
+// x 128 k one contiguous KiB of codes / 128 B of E4M3 bytes, kWBytes = any
+// alignment and K % 16 == 0 by byte loads, the upper 16 k of a half-filled
+// last 32-k group zero).  All run the same arithmetic on the same values:
+// bit-identical results.
+// One workgroup per CU (256 workgroups fill the chip for N = 8192), so two
+// waves per SIMD: the registers go to loads in flight.
+template <bool AV, int NP, int WL>
+__global__ void __launch_bounds__(kSkThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gemm_skinny4(const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
+            const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_sf,
+            const float* __restrict__ w_g, _Float16* __restrict__ y, int B, int N, int K) {
+  constexpr int TP = 2 * NP;                       // token slots
+  constexpr int CL = (kSkHC * TP * 4 + 63) / 64;   // code items per lane and half round
+  static_assert(kSkHC * TP * 2 <= 64, "one scale item per lane and half round");
+  constexpr int kWB = sk_wave_bytes(NP);
+  constexpr int kAop = sk_aop_bytes(NP);   // operand rows at 0, zeros at kAop
+  constexpr int kSc = 2 * kAop;            // activation scales
+  constexpr int kDummy = kWB - 16;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  unsigned char* st = smem + (size_t)wave * kWB;
+  float* red = reinterpret_cast<float*>(smem);   // after the last round
+
+  const int r16 = lane & 15, g = lane >> 4;
+  const int nch = (K + 127) >> 7;
+  const int cnt = wave < nch ? (nch - 1 - wave) / kSkWaves + 1 : 0;   // chunk(m) for m < cnt
+  auto chunk = [&](int m) { return wave + kSkWaves * m; };
+  const int64_t kb2 = K / 2, kb16 = K / 16;
+
+  int nrow[2];                                   // rows past N re-read row N-1 (not stored)
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg) {
+    const int n = blockIdx.x * kSkRows + rg * 16 + r16;
+    nrow[rg] = n < N ? n : N - 1;
+  }
+  // code item j of the lane: (chunk ii of the half, token t, 32-k part s);
+  // its block 2 s + v is operand row 4 s + 2 (t & 1) + v of pair t / 2, read
+  // by the lanes of group s (bytes 8 v .. 8 v + 7 of their 16).  Items past
+  // the last token go to the dummy.
+  int ct[CL], cii[CL], cs[CL], cdst[CL][2];
+#pragma unroll
+  for (int j = 0; j < CL; ++j) {
+    const int item = lane + 64 * j;
+    const int s = item & 3, t = (item >> 2) % TP, ii = (item >> 2) / TP;
+    const bool ok = ii < kSkHC && t < B;
+    ct[j] = t < B ? t : B - 1;
+    cii[j] = ii < kSkHC ? ii : 0;
+    cs[j] = s;
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+      cdst[j][v] = ok ? ((ii * NP + (t >> 1)) * 16 + 4 * s + 2 * (t & 1) + v) * 16 : kDummy;
+  }
+  // scale item of the lane: (ii, token t, half s of the chunk's blocks):
+  // blocks 4 s + 2 u, 4 s + 2 u + 1 go to the scale slot of (ii, pair t / 2,
+  // lane group 2 s + u) at floats 2 (t & 1), 2 (t & 1) + 1
+  int sdst[2];
+  const int ss = lane & 1, stk = (lane >> 1) % TP, sii = (lane >> 1) / TP;
+  const int sto = stk < B ? stk : B - 1;
+  {
+    const bool ok = sii < kSkHC && stk < B;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      sdst[u] = ok ? kSc + ((sii * NP + (stk >> 1)) * 4 + 2 * ss + u) * 16 + 8 * (stk & 1) : kDummy;
+  }
+  const int sii_c = sii < kSkHC ? sii : 0;
+  // the zero rows, written once; operand row r16 of a pair is read from the
+  // stage by lane group r16 / 4 (whose 32 k hold the row's block), from the
+  // zeros by the other three.  Scale slots of tokens past B are never written:
+  // they meet only operand rows of those tokens, whose totals are not stored.
+  for (int o = 16 * lane; o < kAop; o += 1024) *reinterpret_cast<u32x4*>(st + kAop + o) = u32x4{0u, 0u, 0u, 0u};
+  const int abase = ((r16 >> 2) == g ? 0 : kAop) + 16 * r16;
+
+  v2f tot[2][NP];   // per row group and pair: FP32 totals of tokens 2 p, 2 p + 1
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+    for (int p = 0; p < NP; ++p) tot[rg][p] = v2f{0.0f, 0.0f};
+
+  // FULL: all kSkPF chunks of the round inside the wave's list and inside K
+  auto round = [&](int mb, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    u32x4 acode[kSkHalves][CL];
+    v4f ascl[kSkHalves];
+    uint4 wc[kSkPF][2];
+    uint32_t wsv[kSkPF][2];
+    // 1. loads, half by half: the half's activation items, then its weights.
+    //    In a partial round, addresses outside the range or past K are
+    //    clamped to k = 0 and the values are zeroed.
+#pragma unroll
+    for (int h = 0; h < kSkHalves; ++h) {
+#pragma unroll
+      for (int j = 0; j < CL; ++j) {
+        const int mi = mb + kSkHC * h + cii[j];
+        const int k0 = chunk(FULL ? mi : (mi < cnt ? mi : cnt - 1)) * 128 + 32 * cs[j];
+        const uint8_t* pa = a + (int64_t)ct[j] * kb2;
+        if (FULL) {
+          if constexpr (AV) {
+            acode[h][j] = *reinterpret_cast<const u32x4*>(pa + k0 / 2);
+          } else {
+            const uint4 q = load_codes32_bytes(pa + k0 / 2, true);
+            acode[h][j] = u32x4{q.x, q.y, q.z, q.w};
+          }
+        } else {
+          const bool v0 = mi < cnt && k0 < K, v1 = mi < cnt && k0 + 16 < K;
+          const uint8_t* p = pa + (v0 ? k0 / 2 : 0);
+          u32x4 q;
+          if constexpr (AV) {
+            q = *reinterpret_cast<const u32x4*>(p);   // K % 64 == 0: v1 == v0
+          } else {
+            const uint4 r = load_codes32_bytes(p, v1);
+            q = u32x4{r.x, r.y, r.z, r.w};
+          }
+          acode[h][j] = u32x4{v0 ? q.x : 0u, v0 ? q.y : 0u, v1 ? q.z : 0u, v1 ? q.w : 0u};
+        }
+      }
+      {
+        const int mi = mb + kSkHC * h + sii_c;
+        const int kb = chunk(FULL ? mi : (mi < cnt ? mi : cnt - 1)) * 8 + 4 * ss;   // first block
+        const float* ps = a_scale + (int64_t)sto * kb16;
+        if (FULL) {
+          if constexpr (AV) ascl[h] = *reinterpret_cast<const v4f*>(ps + kb);
+          else ascl[h] = v4f{ps[kb], ps[kb + 1], ps[kb + 2], ps[kb + 3]};
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const bool ok = mi < cnt && kb + u < kb16;
+            const float f = ps[ok ? kb + u : 0];
+            ascl[h][u] = ok ? f : 0.0f;
+          }
+        }
+      }
+#pragma unroll
+      for (int ii = 0; ii < kSkHC; ++ii) {
+        const int i = kSkHC * h + ii;
+        const int c = chunk(FULL ? mb + i : (mb + i < cnt ? mb + i : cnt - 1));
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg) {
+          if constexpr (WL == kWTiled) {
+            // tile (row group, chunk), lane order r16 + 16 g (K % 128 == 0)
+            const int64_t t = ((int64_t)(nrow[rg] >> 4) * nch + c) * 64 + lane;
+            wc[i][rg] = *reinterpret_cast<const uint4*>(w + t * 16);
+            wsv[i][rg] = (uint32_t)*reinterpret_cast<const uint16_t*>(w_sf + t * 2);
+          } else {
+            const int k0 = c * 128 + 32 * g;
+            const int k = FULL ? k0 : (k0 < K ? k0 : 0);
+            const uint8_t* wr = w + (int64_t)nrow[rg] * kb2 + k / 2;
+            const uint8_t* sr = w_sf + (int64_t)nrow[rg] * kb16 + k / 16;
+            if constexpr (WL == kWBytes) {
+              const bool full = FULL || k + 16 < K;
+              wc[i][rg] = load_codes32_bytes(wr, full);
+              wsv[i][rg] = (uint32_t)sr[0] | (full ? (uint32_t)sr[1] << 8 : 0u);
+            } else {
+              wc[i][rg] = *reinterpret_cast<const uint4*>(wr);
+              wsv[i][rg] = (uint32_t)*reinterpret_cast<const uint16_t*>(sr);
+            }
+          }
+        }
+      }
+      // issue order = arrival order: keep the halves' load groups apart, and
+      // every load of the round ahead of the first use
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+#pragma unroll
+    for (int h = 0; h < kSkHalves; ++h) {
+      // 2. the half's activation items into their operand positions
+      //    (unconditional stores: a branch would move the loads into it)
+#pragma unroll
+      for (int j = 0; j < CL; ++j) {
+        *reinterpret_cast<u32x4*>(st + cdst[j][0]) = u32x4{acode[h][j].x, acode[h][j].y, 0u, 0u};
+        *reinterpret_cast<u32x4*>(st + cdst[j][1]) = u32x4{0u, 0u, acode[h][j].z, acode[h][j].w};
+      }
+      *reinterpret_cast<v2f*>(st + sdst[0]) = v2f{ascl[h][0], ascl[h][1]};
+      *reinterpret_cast<v2f*>(st + sdst[1]) = v2f{ascl[h][2], ascl[h][3]};
+      __builtin_amdgcn_sched_barrier(0);   // staging first: it waits only for the half's activations
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+      // 3. per chunk and pair one MFMA per row group, scaled into the totals
+#pragma unroll
+      for (int ii = 0; ii < kSkHC; ++ii) {
+        const int i = kSkHC * h + ii;
+        v2f swf[2];   // E4M3 scales of blocks 2 g, 2 g + 1 of each row group's row
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg) {
+          uint32_t sb = wsv[i][rg];
+          if (!FULL) {
+            const int k0 = chunk(mb + i) * 128 + 32 * g;
+            const bool cv = mb + i < cnt;
+            sb = (cv && k0 < K ? (sb & 0xFFu) : 0u) | (cv && k0 + 16 < K ? (sb & 0xFF00u) : 0u);
+          }
+          swf[rg] = __builtin_amdgcn_cvt_pk_f32_fp8((int)sb, false);
+        }
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          const u32x4 aop = *reinterpret_cast<const u32x4*>(st + abase + (ii * NP + p) * 256);
+          const v4f sa = *reinterpret_cast<const v4f*>(st + kSc + ((ii * NP + p) * 4 + g) * 16);
+#pragma unroll
+          for (int rg = 0; rg < 2; ++rg) {
+            const uint4 wq = wc[i][rg];
+            const v4f c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                fp4_op(aop), fp4_op(u32x4{wq.x, wq.y, wq.z, wq.w}), v4f{0.0f, 0.0f, 0.0f, 0.0f}, 4, 4, 0,
+                kScaleOne, 0, kScaleOne);
+            float t0 = tot[rg][p][0], t1 = tot[rg][p][1];
+            t0 = __builtin_fmaf(c[0], swf[rg][0] * sa[0], t0);
+            t0 = __builtin_fmaf(c[1], swf[rg][1] * sa[1], t0);
+            t1 = __builtin_fmaf(c[2], swf[rg][0] * sa[2], t1);
+            t1 = __builtin_fmaf(c[3], swf[rg][1] * sa[3], t1);
+            tot[rg][p] = v2f{t0, t1};
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);   // the next half's staging after this half's reads
+    }
+  };
+
+  int mb = 0;
+  for (; mb + kSkPF <= cnt && (chunk(mb + kSkPF - 1) + 1) * 128 <= K; mb += kSkPF) round(mb, std::true_type{});
+  if (mb < cnt) round(mb, std::false_type{});   // wave-uniform
+
+  // fold the four lane groups' partial totals in registers (every lane ends
+  // with the same sum, added in the same order), then sum the eight K slices
+  // in LDS in a fixed order, scale, round to FP16
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int v = 0; v < 2; ++v) tot[rg][p][v] = fold_lane_groups(tot[rg][p][v]);
+  __syncthreads();   // every wave is done with its stage
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int v = 0; v < 2; ++v)
+        if ((((rg * NP + p) * 2 + v) & 3) == g) red[(wave * TP + 2 * p + v) * kSkRows + rg * 16 + r16] = tot[rg][p][v];
+  __syncthreads();
+  const float gw = *w_g;
+  for (int t = tid; t < TP * kSkRows; t += kSkThreads) {
+    const int b = t / kSkRows, nl = t % kSkRows;
+    const int n = blockIdx.x * kSkRows + nl;
+    if (b < B && n < N) {
+      float s = red[b * kSkRows + nl];
+#pragma unroll
+      for (int q = 1; q < kSkWaves; ++q) s += red[(q * TP + b) * kSkRows + nl];
+      y[(int64_t)b * N + n] = (_Float16)(s * gw);
+    }
+  }
+}
+
+
 constexpr int kSkPitch = kSkPF * 128 + 8;        // halves per staged activation row
 constexpr int kSkRedPitch = kSkRows * 16 + 4;    // floats per wave in the K-slice reduction
 
 // Dynamic LDS of the skinny kernel for IPL activation items per lane: per wave
 // a stage of 4 IPL + 1 rows x kSkPitch halves and as many FP32 powers of two
 // (the K-slice reduction reuses the stages after a barrier).
-constexpr size_t skinny_lds_bytes(int ipl) {
+constexpr size_t skinny16_lds_bytes(int ipl) {
   return (size_t)kSkWaves * (size_t)(4 * ipl + 1) * (kSkPitch * 2 + 4 * kSkHalves);
 }
-static_assert(skinny_lds_bytes(1) >= (size_t)kSkWaves * kSkRedPitch * 4, "reduction fits the stages");
+static_assert(skinny16_lds_bytes(2) >= (size_t)kSkWaves * kSkRedPitch * 4, "reduction fits the stages");
 
-// One workgroup = 32 weight rows x all of K; wave w owns the 128-k chunks
-// [w nch / 8, (w+1) nch / 8) for both 16-row groups, in rounds of kSkPF
+// Decode with more tokens (4 < B <= 16): the weights dequantized once per
+// chunk serve every token through v_mfma_f32_16x16x32_f16, so the
+// arithmetic per weight does not grow with B (the FP4 kernel's scaling
+// epilogue does, by two operations per token, block and row).
+// One workgroup = 32 weight rows x all of K; wave w owns the interleaved
+// 128-k chunks w, w + 8, ... for both 16-row groups, in rounds of kSkPF
 // chunks.  A round:
 //  1. issues its loads half round by half round: the half's activation items
 //     (IPL per lane, each 16 codes of one row and their FP32 combined scale;
@@ -195,7 +528,7 @@ static_assert(skinny_lds_bytes(1) >= (size_t)kSkWaves * kSkRedPitch * 4, "reduct
 // waves per SIMD: the registers go to loads in flight and operand buffers.
 template <bool A4, int IPL, int WL>
 __global__ void __launch_bounds__(kSkThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-gemm_skinny(const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
+gemm_skinny16(const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
             const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_sf,
             const float* __restrict__ w_g, _Float16* __restrict__ y, int B, int N, int K) {
   constexpr int R = 4 * IPL;                  // staged activation rows; row R takes the
@@ -392,20 +725,28 @@ gemm_skinny(const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
 typedef void (*SkinnyFn)(const uint8_t*, const float*, const uint8_t*, const uint8_t*, const float*,
                          _Float16*, int, int, int);
 
-// Activation items per lane covering B rows.
-int skinny_ipl(int B) { return B <= 4 ? 1 : (B <= 8 ? 2 : 4); }
+// B <= 4: the FP4 kernel with NP token pairs; 4 < B <= 16: the FP16 kernel
+// with IPL activation items per lane (B <= 4 IPL).
+constexpr int kSkFp4MaxB = 4;
+int skinny_np(int B) { return B <= 2 ? 1 : 2; }
+int skinny_ipl(int B) { return B <= 8 ? 2 : 4; }
+size_t skinny_lds(int B) { return B <= kSkFp4MaxB ? skinny4_lds_bytes(skinny_np(B)) : skinny16_lds_bytes(skinny_ipl(B)); }
 
-template <bool A4, int WL>
-SkinnyFn skinny_kernel_a(int ipl) {
-  if (ipl == 1) return gemm_skinny<A4, 1, WL>;
-  if (ipl == 2) return gemm_skinny<A4, 2, WL>;
-  return gemm_skinny<A4, 4, WL>;
+template <bool X, int WL>
+SkinnyFn skinny_kernel_x(int B) {
+  if (B <= kSkFp4MaxB) return skinny_np(B) == 1 ? gemm_skinny4<X, 1, WL> : gemm_skinny4<X, 2, WL>;
+  return skinny_ipl(B) == 2 ? gemm_skinny16<X, 2, WL> : gemm_skinny16<X, 4, WL>;
 }
-// The byte-load weight path uses byte loads for the activation codes too.
-SkinnyFn skinny_kernel(bool a4, int ipl, int wl) {
-  if (wl == kWBytes) return skinny_kernel_a<false, kWBytes>(ipl);
-  if (wl == kWTiled) return a4 ? skinny_kernel_a<true, kWTiled>(ipl) : skinny_kernel_a<false, kWTiled>(ipl);
-  return a4 ? skinny_kernel_a<true, kWPlain>(ipl) : skinny_kernel_a<false, kWPlain>(ipl);
+// x: the activation flag of the kernel family (FP4: 16-byte code and scale
+// loads; FP16: 4-byte aligned codes).  The byte-load weight path of the FP16
+// kernel uses byte loads for the activation codes too.
+SkinnyFn skinny_kernel(int B, bool x, int wl) {
+  if (wl == kWBytes) {
+    if (B > kSkFp4MaxB) return skinny_kernel_x<false, kWBytes>(B);
+    return x ? skinny_kernel_x<true, kWBytes>(B) : skinny_kernel_x<false, kWBytes>(B);
+  }
+  if (wl == kWTiled) return x ? skinny_kernel_x<true, kWTiled>(B) : skinny_kernel_x<false, kWTiled>(B);
+  return x ? skinny_kernel_x<true, kWPlain>(B) : skinny_kernel_x<false, kWPlain>(B);
 }
 
 // ------------------------------------------------------------ tiled (prefill)
@@ -847,10 +1188,10 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   std::call_once(once, []() {
     for (int wl = kWPlain; wl <= kWBytes && attr_err == hipSuccess; ++wl)
       for (int a4 = 0; a4 < 2 && attr_err == hipSuccess; ++a4)
-        for (int ipl = 1; ipl <= 4 && attr_err == hipSuccess; ipl *= 2)
-          attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(skinny_kernel(a4 != 0, ipl, wl)),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)skinny_lds_bytes(ipl));
+        for (int B : {1, 3, 5, 9})   // one B per kernel instance
+          if (attr_err == hipSuccess)
+            attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(skinny_kernel(B, a4 != 0, wl)),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)skinny_lds(B));
     if (attr_err == hipSuccess)
       attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled<false>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTiledLds);
@@ -867,9 +1208,13 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   const int wl = g.tiled ? kWTiled : (w_rows16 ? kWPlain : kWBytes);
   if (use_skinny(g.B)) {
     const unsigned grid = (unsigned)((N + kSkRows - 1) / kSkRows);
-    const int ipl = skinny_ipl(B);
-    const SkinnyFn fn = skinny_kernel(((uintptr_t)g.a % 4) == 0, ipl, wl);
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(kSkThreads), skinny_lds_bytes(ipl), s, g.a, g.a_scale, g.w,
+    // FP4 kernel: 16-byte activation code and scale loads (16-byte aligned
+    // rows and bases); FP16 kernel: 4-byte aligned activation codes
+    const bool x = B <= kSkFp4MaxB
+                       ? ((uintptr_t)g.a % 16) == 0 && ((uintptr_t)g.a_scale % 16) == 0 && K % 64 == 0
+                       : ((uintptr_t)g.a % 4) == 0;
+    const SkinnyFn fn = skinny_kernel(B, x, wl);
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(kSkThreads), skinny_lds(B), s, g.a, g.a_scale, g.w,
                        g.w_sf, g.w_g, y, B, N, K);
     return hipGetLastError();
   }

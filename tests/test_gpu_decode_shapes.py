@@ -1,10 +1,13 @@
-"""Decode GEMM (gemm_skinny, B <= 16) over the shapes that exercise its work
-split: each wave owns every eighth 128-k chunk of K and processes them in
-rounds of four, with two activation groups of two chunks per round.  Shapes
-cover waves without chunks (K < 1024), a partial last chunk (K % 128 != 0),
-K % 32 == 16 (weights on the byte-load path), full and partial rounds,
-several rounds per wave (K = 16384), ragged N, and B in each of the three
-activation-item widths (B <= 4, <= 8, <= 16).  Operands are oracle-quantized
+"""Decode GEMM (B <= 16: gemm_skinny4 on the FP4 matrix cores for B <= 4,
+gemm_skinny16 on dequantized FP16 weights above) over the shapes that
+exercise their work split: each wave owns every eighth 128-k chunk of K and
+processes them in rounds of four, with two activation groups of two chunks
+per round.  Shapes cover waves without chunks (K < 1024), a partial last
+chunk (K % 128 != 0, with K % 64 == 0 on the FP4 kernel's 16-byte activation
+loads and K % 64 == 32 on its byte loads), K % 32 == 16 (weights on the
+byte-load path), full and partial rounds, several rounds per wave
+(K = 16384), ragged N, one and two token pairs of the FP4 kernel, and both
+activation-item widths of the FP16 kernel (B <= 8, <= 16).  Operands are oracle-quantized
 from seeded bf16 data ("Fused Nvfp4 GEMM All Reduce Plugin", Baked-weight
 inputs); every element is checked against the fp64 oracle within the bound of
 the arithmetic, and the weight layouts (plain rows, byte loads at an odd
@@ -32,7 +35,10 @@ SHAPES = [(1, 32, 16),          # one partial chunk; seven waves without chunks
           (2, 40, 48),          # K % 32 == 16: byte-load weights
           (4, 96, 640),         # five chunks: one partial round per wave
           (3, 17, 1024),        # ragged N, one chunk per wave
-          (5, 64, 4096),        # two item widths, one full round per wave
+          (2, 96, 4096 + 64),   # FP4 kernel: partial last chunk, 16-byte activation loads
+          (4, 256, 4224),       # FP4 kernel, two pairs: a full and a partial round on wave 0
+          (1, 64, 2048 + 32),   # FP4 kernel: partial last chunk, byte activation loads
+          (5, 64, 4096),        # FP16 kernel: one full round per wave
           (8, 256, 4224),       # 33 chunks: a full and a partial round on wave 0
           (13, 48, 8192 + 32),  # widest items, partial last chunk
           (16, 1040, 16384)]    # four rounds per wave, N not a multiple of 32
