@@ -480,7 +480,8 @@ gemm_skinny4(const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
 
 
 constexpr int kSkPitch = kSkPF * 128 + 8;        // halves per staged activation row
-constexpr int kSkRedPitch = kSkRows * 16 + 4;    // floats per wave in the K-slice reduction
+constexpr int kSkRedRow = kSkRows + 1;          // K-slice reduction: [wave][token][row], rows padded
+constexpr int kSkRedPitch = 16 * kSkRedRow;      // floats per wave
 
 // Dynamic LDS of the skinny kernel for IPL activation items per lane: per wave
 // a stage of 4 IPL + 1 rows x kSkPitch halves and as many FP32 powers of two
@@ -707,16 +708,16 @@ gemm_skinny16(const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
 #pragma unroll
   for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave * kSkRedPitch + (rg * 16 + 4 * g + r) * 16 + r16] = tot[rg][r];
+    for (int r = 0; r < 4; ++r) red[wave * kSkRedPitch + r16 * kSkRedRow + rg * 16 + 4 * g + r] = tot[rg][r];
   __syncthreads();
   const float gw = *w_g;
-  for (int t = tid; t < 16 * kSkRows; t += kSkThreads) {
+  for (int t = tid; t < B * kSkRows; t += kSkThreads) {
     const int b = t / kSkRows, nl = t % kSkRows;
     const int n = blockIdx.x * kSkRows + nl;
-    if (b < B && n < N) {
-      float s = red[nl * 16 + b];
+    if (n < N) {
+      float s = red[b * kSkRedRow + nl];
 #pragma unroll
-      for (int q = 1; q < kSkWaves; ++q) s += red[q * kSkRedPitch + nl * 16 + b];
+      for (int q = 1; q < kSkWaves; ++q) s += red[q * kSkRedPitch + b * kSkRedRow + nl];
       y[(int64_t)b * N + n] = (_Float16)(s * gw);
     }
   }
