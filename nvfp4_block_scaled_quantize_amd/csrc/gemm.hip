@@ -753,16 +753,44 @@ SkinnyFn skinny_kernel(int B, bool x, int wl) {
 // ------------------------------------------------------------ tiled (prefill)
 
 // Prologue: one workgroup per activation row -> normalized FP16 row and its
-// power of two.
+// power of two.  Rows of up to 256 * kA16Items blocks keep every block's
+// combined scale and codes in registers, loaded before the row maximum is
+// formed (one pass over the row, all loads in flight together); longer rows
+// take a second pass.  A8: activation codes 8-byte aligned (one dwordx2 load
+// per block), else byte loads.  The same arithmetic either way.
+constexpr int kA16Items = 4;
+template <bool A8>
 __global__ void __launch_bounds__(256)
 a_to_f16_rows(const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
               _Float16* __restrict__ a16, float* __restrict__ rowscale, int K) {
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
-  const int64_t kb16 = K / 16;
+  const int kb16 = K / 16;
   const float* sc = a_scale + row * kb16;
+  const uint8_t* ar = a + row * (K / 2);
+  _Float16* out = a16 + row * K;
+  auto codes8 = [&](int j) -> u32x2 {
+    if constexpr (A8) return *reinterpret_cast<const u32x2*>(ar + 8 * j);
+    else return u32x2{load_u32_bytes(ar + 8 * j), load_u32_bytes(ar + 8 * j + 4)};
+  };
+  const bool held = kb16 <= 256 * kA16Items;   // block-uniform
+  float cs[kA16Items];
+  u32x2 cc[kA16Items];
   float m = 0.0f;
-  for (int64_t j = threadIdx.x; j < kb16; j += 256) m = __builtin_fmaxf(m, sc[j]);
+  if (held) {
+#pragma unroll
+    for (int i = 0; i < kA16Items; ++i) {
+      const int j = threadIdx.x + 256 * i;
+      const int jj = j < kb16 ? j : 0;
+      cs[i] = sc[jj];
+      cc[i] = codes8(jj);
+    }
+#pragma unroll
+    for (int i = 0; i < kA16Items; ++i)
+      if (threadIdx.x + 256 * i < kb16) m = __builtin_fmaxf(m, cs[i]);
+  } else {
+    for (int j = threadIdx.x; j < kb16; j += 256) m = __builtin_fmaxf(m, sc[j]);
+  }
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
@@ -770,13 +798,23 @@ a_to_f16_rows(const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
   const int e = row_exponent(m);
   const float inv = __builtin_ldexpf(1.0f, -e);
   if (threadIdx.x == 0) rowscale[row] = __builtin_ldexpf(1.0f, e);
-  const uint8_t* ar = a + row * (K / 2);
-  for (int64_t j = threadIdx.x; j < kb16; j += 256) {
-    const float c = sc[j] * inv;
-    const uint32_t c0 = load_u32_bytes(ar + 8 * j), c1 = load_u32_bytes(ar + 8 * j + 4);
-    _Float16* out = a16 + row * K + 16 * j;
-    *reinterpret_cast<v8h*>(out) = dequant8_act(c0, c);
-    *reinterpret_cast<v8h*>(out + 8) = dequant8_act(c1, c);
+  if (held) {
+#pragma unroll
+    for (int i = 0; i < kA16Items; ++i) {
+      const int j = threadIdx.x + 256 * i;
+      if (j < kb16) {
+        const float c = cs[i] * inv;
+        *reinterpret_cast<v8h*>(out + 16 * j) = dequant8_act(cc[i][0], c);
+        *reinterpret_cast<v8h*>(out + 16 * j + 8) = dequant8_act(cc[i][1], c);
+      }
+    }
+  } else {
+    for (int j = threadIdx.x; j < kb16; j += 256) {
+      const float c = sc[j] * inv;
+      const u32x2 q = codes8(j);
+      *reinterpret_cast<v8h*>(out + 16 * j) = dequant8_act(q[0], c);
+      *reinterpret_cast<v8h*>(out + 16 * j + 8) = dequant8_act(q[1], c);
+    }
   }
 }
 
@@ -1224,8 +1262,10 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   float* rowscale = reinterpret_cast<float*>(ws + align256((size_t)B * (size_t)K * 2));
   // gemm_wide's copies take 32-bit lane offsets of up to 512 rows x K bytes
   const bool wide = g.tiled || (w_rows16 && K % kTK == 0 && ((uintptr_t)g.w_sf % 4) == 0 && g.K <= (1 << 24));
-  hipLaunchKernelGGL(a_to_f16_rows, dim3((unsigned)B), dim3(256), 0, s, g.a, g.a_scale, a16,
-                     rowscale, K);
+  if ((uintptr_t)g.a % 8 == 0)
+    hipLaunchKernelGGL(a_to_f16_rows<true>, dim3((unsigned)B), dim3(256), 0, s, g.a, g.a_scale, a16, rowscale, K);
+  else
+    hipLaunchKernelGGL(a_to_f16_rows<false>, dim3((unsigned)B), dim3(256), 0, s, g.a, g.a_scale, a16, rowscale, K);
   if (wide) {
     const int wtm = (B + kXM - 1) / kXM, wtn = (N + kXN - 1) / kXN;
     if (g.tiled)

@@ -163,8 +163,11 @@ def test_c5_expert_weights_quantize_bit_exact(nv, oracle, which):
 
 # ---------------------------------------------------------------- boundary paths
 
-@pytest.mark.parametrize("B,N,K", [(1, 96, 256), (8, 8192, 4096), (13, 64, 528)])
-def test_decode_activation_codes_at_2_byte_offset(nv, oracle, B, N, K):
+# decode shapes, and prefill shapes whose FP16 prologue keeps a row in
+# registers (K <= 16384) or takes two passes over it (K = 16640)
+@pytest.mark.parametrize("B,N,K", [(1, 96, 256), (8, 8192, 4096), (13, 64, 528), (40, 64, 1024),
+                                   (24, 64, 16384 + 256)])
+def test_activation_codes_at_2_byte_offset(nv, oracle, B, N, K):
     d = si.random_nvfp4_operands(B, N, K, seed=B + K)
     t = {k: torch.from_numpy(v).cuda() for k, v in d.items()}
     y0 = nv.gemm(t["a_codes"], t["a_scale"], t["w_codes"], t["w_sf"], t["w_g"])
