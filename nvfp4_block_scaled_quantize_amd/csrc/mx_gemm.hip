@@ -335,8 +335,12 @@ mx_gemm_skinny(const uint8_t* __restrict__ a, const uint8_t* __restrict__ as,
   const int c0 = wave * nch / kMsWaves, c1 = (wave + 1) * nch / kMsWaves;
   const uint8_t* wg_codes = w + (size_t)g * K * 16 + 16 * lane;
   const uint8_t* wg_scales = ws + (size_t)g * K + 2 * lane;
-  const uint8_t* a_codes = a + 16 * lane;
-  const uint8_t* a_scales = as + 2 * lane;
+  // activation columns past B (padding rows of the tile) read column 0 of
+  // their half instead: the same addresses as that lane, one cache line per
+  // load; their outputs are not stored
+  const int alane = (lane & 31) < B ? lane : (lane & 32);
+  const uint8_t* a_codes = a + 16 * alane;
+  const uint8_t* a_scales = as + 2 * alane;
   v16f acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
