@@ -250,11 +250,20 @@ def run_moe(torch, nv, si, iters=None):
     ws = torch.empty(nv.moe_workspace_size(T, E, c["top_k"], Hd, I), dtype=torch.uint8, device=dev)
     kw = dict(top_k=c["top_k"], n_group=c["n_group"], topk_group=c["topk_group"],
               norm_topk_prob=c["norm_topk_prob"], routed_scaling=c["routed_scaling"], out=out, workspace=ws)
-    ms = graph_time_ms(torch, [(lambda st=st: nv.moe_w4a16(*st, **kw)) for st in sets], reps=3)
+    ms_plain = graph_time_ms(torch, [(lambda st=st: nv.moe_w4a16(*st, **kw)) for st in sets], reps=3)
+    # the same expert weights pre-tiled offline (moe_pretile_weights): the timed layer
+    tiled = []
+    for st in sets:
+        w1t, s1t = nv.moe_pretile_weights(st[3], st[4])
+        w2t, s2t = nv.moe_pretile_weights(st[6], st[7])
+        tiled.append(st[:3] + [w1t, s1t, st[5], w2t, s2t, st[8]])
+    del sets
+    ms = graph_time_ms(torch, [(lambda st=st: nv.moe_w4a16_pretiled(*st, **kw)) for st in tiled], reps=3)
     wbytes = E * (I * Hd // 2 + I * Hd // 16 + Hd * I // 2 + Hd * I // 16) + 2 * E * 4
     by = wbytes + T * Hd * 2 * 2 + T * E * 4 + E * 4
     return dict(T=T, E=E, us=ms * 1e3, bytes=by, GBps=by / (ms * 1e-3) / 1e9,
-                hbm_frac=by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, flops=2.0 * T * c["top_k"] * (2 * Hd * I))
+                hbm_frac=by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, flops=2.0 * T * c["top_k"] * (2 * Hd * I),
+                weights="pre-tiled", us_plain_weights=ms_plain * 1e3)
 
 
 def mx_gemm_bytes(B, N, K):

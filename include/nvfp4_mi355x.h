@@ -243,6 +243,28 @@ size_t nvfp4_moe_w4a16_workspace_size(int32_t tokens, int32_t experts, int32_t t
                                       int32_t inter);
 
 /*
+ * nvfp4_moe_w4a16_pretiled -- nvfp4_moe_w4a16 with the expert weights in the
+ * pre-tiled layout (offline weight preparation, as for nvfp4_gemm_pretiled):
+ *   w1, w1_sf : nvfp4_pretile_weight of the stacked fc1 weights viewed as one
+ *               [experts * inter, hidden] matrix (codes [experts * inter,
+ *               hidden/2], E4M3 bytes [experts * inter, hidden/16])
+ *   w2, w2_sf : the same of the stacked fc2 weights [experts * hidden, inter]
+ * A 16-row group never spans two experts, so expert e's tiles are the bytes
+ * at the same offsets as its rows in the plain layout.  Same routing,
+ * arithmetic and results as nvfp4_moe_w4a16 (bit-identical output), same
+ * workspace.  Requires hidden % 128 == 0 and inter % 128 == 0 besides the
+ * conditions of nvfp4_moe_w4a16 (EINVAL otherwise).
+ */
+int32_t nvfp4_moe_w4a16_pretiled(const float* router_logits, const float* correction_bias,
+                                 const void* x, const uint8_t* w1, const uint8_t* w1_sf,
+                                 const float* w1_g, const uint8_t* w2, const uint8_t* w2_sf,
+                                 const float* w2_g, void* out, int32_t* topk_ids_out,
+                                 float* topk_w_out, int32_t tokens, int32_t experts, int32_t top_k,
+                                 int32_t hidden, int32_t inter, int32_t n_group,
+                                 int32_t topk_group, int32_t norm_topk_prob, float routed_scaling,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * nvfp4_moe_w4a16_noalloc -- nvfp4_moe_w4a16 for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc): the same arguments without the workspace, the same

@@ -25,7 +25,7 @@ EXPORTS = [
     "nvfp4_gemm", "nvfp4_gemm_workspace_size", "nvfp4_moe_w4a16", "nvfp4_moe_w4a16_workspace_size",
     "nvfp4_register_weight", "nvfp4_unregister_weight", "nvfp4_gemm_external",
     "nvfp4_pretile_weight", "nvfp4_gemm_pretiled", "nvfp4_mx_quantize", "nvfp4_mx_tile",
-    "nvfp4_mx_gemm", "nvfp4_moe_w4a16_noalloc",
+    "nvfp4_mx_gemm", "nvfp4_moe_w4a16_noalloc", "nvfp4_moe_w4a16_pretiled",
 ]
 MX_ROWS, MX_TILED = 0, 1
 
@@ -57,6 +57,9 @@ def _load() -> ctypes.CDLL:
     L.nvfp4_moe_w4a16.argtypes = [p, p, p, p, p, p, p, p, p, p, p, p,
                                   i32, i32, i32, i32, i32, i32, i32, i32, f32, p, sz, p]
     L.nvfp4_moe_w4a16.restype = i32
+    L.nvfp4_moe_w4a16_pretiled.argtypes = [p, p, p, p, p, p, p, p, p, p, p, p,
+                                           i32, i32, i32, i32, i32, i32, i32, i32, f32, p, sz, p]
+    L.nvfp4_moe_w4a16_pretiled.restype = i32
     L.nvfp4_moe_w4a16_noalloc.argtypes = [p, p, p, p, p, p, p, p, p, p, p, p,
                                           i32, i32, i32, i32, i32, i32, i32, i32, f32, p]
     L.nvfp4_moe_w4a16_noalloc.restype = i32
@@ -327,6 +330,36 @@ def moe_w4a16(logits, bias, x, w1, w1_sf, w1_g, w2, w2_sf, w2_g, top_k, n_group,
               norm_topk_prob=True, routed_scaling=1.0, out=None, want_routing=False,
               workspace=None, stream=None):
     """Routed W4A16 MoE layer; returns out (and (ids, weights) if want_routing)."""
+    return _moe(_lib.nvfp4_moe_w4a16, "nvfp4_moe_w4a16", logits, bias, x, w1, w1_sf, w1_g, w2, w2_sf,
+                w2_g, top_k, n_group, topk_group, norm_topk_prob, routed_scaling, out, want_routing,
+                workspace, stream)
+
+
+def moe_pretile_weights(w: torch.Tensor, w_sf: torch.Tensor, stream=None) -> tuple:
+    """The pre-tiled layout of stacked expert weights [E, N, K/2] codes and
+    [E, N, K/16] E4M3 bytes (nvfp4_pretile_weight of the [E*N, K] matrix),
+    returned with the same shapes."""
+    if not isinstance(w, torch.Tensor) or w.dim() != 3:
+        raise ValueError("w must be a 3-D tensor [experts, rows, K/2]")
+    E, N, K2 = w.shape
+    _need(w, "w", torch.uint8)
+    _need(w_sf, "w_sf", torch.uint8, (E, N, K2 // 8))
+    t = pretile_weight(w.reshape(E * N, K2), w_sf.reshape(E * N, K2 // 8), stream=stream)
+    return t["codes"].view(E, N, K2), t["sf"].view(E, N, K2 // 8)
+
+
+def moe_w4a16_pretiled(logits, bias, x, w1, w1_sf, w1_g, w2, w2_sf, w2_g, top_k, n_group, topk_group,
+                       norm_topk_prob=True, routed_scaling=1.0, out=None, want_routing=False,
+                       workspace=None, stream=None):
+    """moe_w4a16() with w1/w1_sf and w2/w2_sf from moe_pretile_weights()
+    (same shapes and results)."""
+    return _moe(_lib.nvfp4_moe_w4a16_pretiled, "nvfp4_moe_w4a16_pretiled", logits, bias, x, w1, w1_sf,
+                w1_g, w2, w2_sf, w2_g, top_k, n_group, topk_group, norm_topk_prob, routed_scaling, out,
+                want_routing, workspace, stream)
+
+
+def _moe(fn, name, logits, bias, x, w1, w1_sf, w1_g, w2, w2_sf, w2_g, top_k, n_group, topk_group,
+         norm_topk_prob, routed_scaling, out, want_routing, workspace, stream):
     _need_2d(logits, "logits")
     _need_2d(x, "x")
     T, E = logits.shape
@@ -350,12 +383,12 @@ def moe_w4a16(logits, bias, x, w1, w1_sf, w1_g, w2, w2_sf, w2_g, top_k, n_group,
     ids = torch.empty((T, top_k), dtype=torch.int32, device=x.device) if want_routing else None
     wts = torch.empty((T, top_k), dtype=torch.float32, device=x.device) if want_routing else None
     ws, wsb = _workspace(moe_workspace_size(T, E, top_k, hidden, inter), x.device, workspace)
-    st = _lib.nvfp4_moe_w4a16(_ptr(logits), _ptr(bias), _ptr(x), _ptr(w1), _ptr(w1_sf), _ptr(w1_g),
-                              _ptr(w2), _ptr(w2_sf), _ptr(w2_g), _ptr(o), _ptr(ids), _ptr(wts),
-                              T, E, top_k, hidden, inter, n_group, topk_group, int(bool(norm_topk_prob)),
-                              float(routed_scaling), _ptr(ws), wsb, _stream(stream))
+    st = fn(_ptr(logits), _ptr(bias), _ptr(x), _ptr(w1), _ptr(w1_sf), _ptr(w1_g),
+            _ptr(w2), _ptr(w2_sf), _ptr(w2_g), _ptr(o), _ptr(ids), _ptr(wts),
+            T, E, top_k, hidden, inter, n_group, topk_group, int(bool(norm_topk_prob)),
+            float(routed_scaling), _ptr(ws), wsb, _stream(stream))
     if st != NVFP4_OK:
-        raise Nvfp4Error(st, "nvfp4_moe_w4a16")
+        raise Nvfp4Error(st, name)
     return (o, ids, wts) if want_routing else o
 
 

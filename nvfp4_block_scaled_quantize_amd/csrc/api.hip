@@ -346,7 +346,31 @@ int32_t nvfp4_moe_w4a16(const float* router_logits, const float* correction_bias
   nvfp4::MoeArgs m{router_logits, correction_bias, x, w1, w1_sf, w1_g, w2, w2_sf, w2_g, out,
                    topk_ids_out, topk_w_out, tokens, experts, top_k, hidden, inter, n_group,
                    topk_group, norm_topk_prob ? 1 : 0, routed_scaling, workspace, workspace_bytes,
-                   current_device()->num_cus};
+                   current_device()->num_cus, 0};
+  return hip_status(nvfp4::launch_moe(m, (hipStream_t)stream));
+}
+
+int32_t nvfp4_moe_w4a16_pretiled(const float* router_logits, const float* correction_bias,
+                                 const void* x, const uint8_t* w1, const uint8_t* w1_sf,
+                                 const float* w1_g, const uint8_t* w2, const uint8_t* w2_sf,
+                                 const float* w2_g, void* out, int32_t* topk_ids_out,
+                                 float* topk_w_out, int32_t tokens, int32_t experts, int32_t top_k,
+                                 int32_t hidden, int32_t inter, int32_t n_group,
+                                 int32_t topk_group, int32_t norm_topk_prob, float routed_scaling,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  const int32_t st = moe_check(router_logits, correction_bias, x, w1, w1_sf, w1_g, w2, w2_sf, w2_g,
+                               out, tokens, experts, top_k, hidden, inter, n_group, topk_group);
+  if (st != NVFP4_OK) return st;
+  if (hidden % 128 != 0 || inter % 128 != 0) return NVFP4_EINVAL;   // whole 128-k chunks
+  if (tokens == 0) return NVFP4_OK;
+  const size_t need = nvfp4::moe_workspace_bytes(tokens, experts, top_k, hidden, inter);
+  if (!workspace || workspace_bytes < need || !aligned256(workspace)) return NVFP4_EWORKSPACE;
+  const int32_t ds = device_status();
+  if (ds != NVFP4_OK) return ds;
+  nvfp4::MoeArgs m{router_logits, correction_bias, x, w1, w1_sf, w1_g, w2, w2_sf, w2_g, out,
+                   topk_ids_out, topk_w_out, tokens, experts, top_k, hidden, inter, n_group,
+                   topk_group, norm_topk_prob ? 1 : 0, routed_scaling, workspace, workspace_bytes,
+                   current_device()->num_cus, 1};
   return hip_status(nvfp4::launch_moe(m, (hipStream_t)stream));
 }
 
@@ -371,7 +395,7 @@ int32_t nvfp4_moe_w4a16_noalloc(const float* router_logits, const float* correct
   nvfp4::MoeArgs m{router_logits, correction_bias, x, w1, w1_sf, w1_g, w2, w2_sf, w2_g, out,
                    topk_ids_out, topk_w_out, tokens, experts, top_k, hidden, inter, n_group,
                    topk_group, norm_topk_prob ? 1 : 0, routed_scaling, scratch, scratch_bytes,
-                   current_device()->num_cus};
+                   current_device()->num_cus, 0};
   return hip_status(nvfp4::launch_moe(m, (hipStream_t)stream));
 }
 

@@ -70,6 +70,7 @@ struct MoeArgs {
   void* workspace;
   size_t workspace_bytes;
   int num_cus;         // compute units of the current device (work split)
+  int tiled_weights;   // w1/w2 codes and E4M3 bytes in the pre-tiled layout
 };
 
 // MXFP4 variant: the MX tile permutation and the block-scaled MFMA GEMM.

@@ -21,6 +21,9 @@
 //                  2^-et per (pair, 128-row tile), et the exponent of the
 //                  tile's largest h; the pair's overall largest h is an
 //                  integer max of fp32 bits (order independent).
+//                  Weights in the plain [E, N, K/2] layout or pre-tiled
+//                  (nvfp4_pretile_weight of the stacked [E N, K] matrix), in
+//                  which each 64-k stage of a unit is whole cache lines.
 //  4. fc2        : the same units on h.  The activations of each 128-k
 //                  range (one fc1 tile) are multiplied by 2^(et - e) in FP16,
 //                  e = exponent of the pair's largest h; o = acc * g2 * 2^e
@@ -317,6 +320,15 @@ __device__ __forceinline__ v8h dequant8_w(uint32_t codes, _Float16 s16) {
 // 16 distinct bank groups, and 8 lanes 8):
 //   codes: 32 B per row, piece j of row r at j ^ (((r >> 2) ^ (r >> 3)) & 1);
 //   E4M3 bytes: 4 B per row;
+//   TW (weights in the pre-tiled layout of nvfp4_pretile_weight, applied to
+//   the stacked [E N, K] matrix: per 16-row group and 128-k chunk 1 KiB of
+//   codes, lane l = r + 16 g holding row r, k = 32 g .. 32 g + 31, and 128 B
+//   of E4M3 pairs in the same lane order): a stage is the half of each of
+//   its eight groups' tiles, 512 B of codes and 64 B of E4M3 bytes each,
+//   copied as they are (a stage is then 36 whole cache lines instead of
+//   touching 128 rows' lines twice): codes piece h of row r at
+//   32 (r / 16) + 16 h + r % 16, the pair of bytes at 64 (r / 16) + 32 h +
+//   2 (r % 16);
 //   activations: 128 B per token slot, piece j of slot s at (j + rot(s)) mod
 //   8, rot(s) = s + (s / 8) mod 4 (the same for slots s and s + 32) -- a
 //   lane's four pieces of a stage are its slot base plus a constant, minus
@@ -368,7 +380,7 @@ __device__ __forceinline__ void wait_vmcnt_rt(int n) {
   }
 }
 
-template <int FC>
+template <int FC, bool TW>
 __global__ void __launch_bounds__(kMfThreads, 3)
 moe_fc(const _Float16* __restrict__ act, const int32_t* __restrict__ plists,
        const int32_t* __restrict__ tlists, const int32_t* __restrict__ counts, int T,
@@ -411,19 +423,36 @@ moe_fc(const _Float16* __restrict__ act, const int32_t* __restrict__ plists,
   // the stage (row (i * 128 + ct) / 2), the E4M3 copy the dword of row ct;
   // rows past N re-read row N - 1 (their results are not stored)
   uint32_t cofs[2], sofs;
+  constexpr uint32_t kCStep = TW ? 512u : 32u, kSStep = TW ? 64u : 4u;   // bytes per stage
+  if constexpr (TW) {
+    // piece i * 128 + ct of the stage: group G = piece / 32, tile lane
+    // 32 (c % 2) + piece % 32; the stage's offset in a tile is 512 c mod
+    // 1 KiB plus 1 KiB per chunk, i.e. 512 c (64 c for the E4M3 pairs).
+    // Groups past N re-read the last group (their results are not stored).
+    const uint32_t nch2 = (uint32_t)(K / 128), gl = (uint32_t)(N / 16 - 1);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int pos = i * 128 + ct, r = pos >> 1;
-    const int j = (pos & 1) ^ (((r >> 2) ^ (r >> 3)) & 1);
-    const uint32_t n = (uint32_t)(n0 + r < N ? n0 + r : N - 1);
-    cofs[i] = n * (uint32_t)(K / 2) + 16u * j;
+    for (int i = 0; i < 2; ++i) {
+      const int pos = i * 128 + ct;
+      const uint32_t gg = (uint32_t)(n0 / 16 + (pos >> 5));
+      cofs[i] = (gg < gl ? gg : gl) * nch2 * 1024u + 16u * (uint32_t)(pos & 31);
+    }
+    const uint32_t gs = (uint32_t)(n0 / 16 + (ct >> 4));
+    sofs = (gs < gl ? gs : gl) * nch2 * 128u + 4u * (uint32_t)(ct & 15);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int pos = i * 128 + ct, r = pos >> 1;
+      const int j = (pos & 1) ^ (((r >> 2) ^ (r >> 3)) & 1);
+      const uint32_t n = (uint32_t)(n0 + r < N ? n0 + r : N - 1);
+      cofs[i] = n * (uint32_t)(K / 2) + 16u * j;
+    }
+    sofs = (uint32_t)(n0 + ct < N ? n0 + ct : N - 1) * (uint32_t)(K / 16);
   }
-  sofs = (uint32_t)(n0 + ct < N ? n0 + ct : N - 1) * (uint32_t)(K / 16);
   auto issue_w = [&](int c) __attribute__((always_inline)) {
     const uint32_t lb = l0 + (c % kMfWBufs) * kMfWB;
-    dma16(we, cofs[0] + 32u * c, lb + 16 * (0 * 128 + 64 * wave));
-    dma16(we, cofs[1] + 32u * c, lb + 16 * (1 * 128 + 64 * wave));
-    dma4(se, sofs + 4u * c, lb + kMfCodeB + 4 * 64 * wave);
+    dma16(we, cofs[0] + kCStep * c, lb + 16 * (0 * 128 + 64 * wave));
+    dma16(we, cofs[1] + kCStep * c, lb + 16 * (1 * 128 + 64 * wave));
+    dma4(se, sofs + kSStep * c, lb + kMfCodeB + 4 * 64 * wave);
   };
 
   const bool first_z = z0 == 0;
@@ -454,8 +483,11 @@ moe_fc(const _Float16* __restrict__ act, const int32_t* __restrict__ plists,
   }
   // operand read offsets (bytes within a stage buffer)
   const int r = 32 * wave + r32;
-  const uint32_t ca = 16u * (2 * r + (h ^ (((r >> 2) ^ (r >> 3)) & 1)));   // code piece h of row r
-  const uint32_t sa = kMfCodeB + 4u * r;                                    // E4M3 dword of row r
+  // code piece h of row r; the E4M3 dword of row r (plain) or its pair for
+  // this lane's 32 k (TW)
+  const uint32_t ca = TW ? 16u * (32 * (r >> 4) + 16 * h + (r & 15))
+                         : 16u * (2 * r + (h ^ (((r >> 2) ^ (r >> 3)) & 1)));
+  const uint32_t sa = TW ? kMfCodeB + 64u * (r >> 4) + 32u * h + 2u * (r & 15) : kMfCodeB + 4u * r;
   const int rot = (r32 + ((r32 >> 3) & 3)) & 7;  // rotation of slots r32 and 32 + r32
   const int b4 = (4 * h + rot) & 7;              // position of the lane's first piece
   const uint32_t ab0 = 128u * r32 + 16u * b4;    // slot r32 of tile 0, piece 4h
@@ -545,7 +577,9 @@ moe_fc(const _Float16* __restrict__ act, const int32_t* __restrict__ plists,
       asm volatile("" : "+v"(bw), "+v"(b0), "+v"(b1));
       const lptr pw = (lptr)(uintptr_t)bw;
       const u32x4 cw = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(pw + ca);
-      const uint32_t sw = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(pw + sa);
+      uint32_t sw;
+      if constexpr (TW) sw = *reinterpret_cast<const __attribute__((address_space(3))) uint16_t*>(pw + sa);
+      else sw = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(pw + sa);
       v8h bf[4][NW];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -556,7 +590,8 @@ moe_fc(const _Float16* __restrict__ act, const int32_t* __restrict__ plists,
       }
       __builtin_amdgcn_sched_barrier(0);
       // this lane's two 16-blocks: bytes 2h and 2h + 1 of the row's dword
-      const uint32_t sh = sw >> (16 * h);
+      // (TW: the pair itself)
+      const uint32_t sh = TW ? sw : sw >> (16 * h);
       const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)sh, 0);
       const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)sh, 1);
 #pragma unroll
@@ -736,11 +771,13 @@ hipError_t launch_moe(const MoeArgs& m, hipStream_t s) {
   const int zt = (m.tokens + kMfTok - 1) / kMfTok;
   const int zs = zt < kMfMaxZ ? zt : kMfMaxZ;
   const int t1 = (m.inter + kMfRows - 1) / kMfRows, t2 = (m.hidden + kMfRows - 1) / kMfRows;
-  hipLaunchKernelGGL(moe_fc<1>, dim3(t1 * zs, m.experts), dim3(kMfThreads), 0, s,
+  auto fc1 = m.tiled_weights ? moe_fc<1, true> : moe_fc<1, false>;
+  auto fc2 = m.tiled_weights ? moe_fc<2, true> : moe_fc<2, false>;
+  hipLaunchKernelGGL(fc1, dim3(t1 * zs, m.experts), dim3(kMfThreads), 0, s,
                      reinterpret_cast<const _Float16*>(m.x), ws.plists, ws.tlists, ws.counts, m.tokens,
                      ws.pmax, ws.etile, nt1, t1, m.w1, m.w1_sf, m.w1_g, m.inter, m.hidden,
                      reinterpret_cast<void*>(ws.h));
-  hipLaunchKernelGGL(moe_fc<2>, dim3(t2 * zs, m.experts), dim3(kMfThreads), 0, s, ws.h, ws.plists,
+  hipLaunchKernelGGL(fc2, dim3(t2 * zs, m.experts), dim3(kMfThreads), 0, s, ws.h, ws.plists,
                      ws.tlists, ws.counts, m.tokens, ws.pmax, ws.etile, nt1, t2, m.w2, m.w2_sf, m.w2_g,
                      m.hidden, m.inter, reinterpret_cast<void*>(ws.o));
   hipLaunchKernelGGL(moe_combine4, dim3(m.tokens, (m.hidden + 1023) / 1024), dim3(256), 0, s, ws.o,

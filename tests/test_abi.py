@@ -102,6 +102,12 @@ def test_moe_validation_without_gpu(nv):
     assert L.nvfp4_moe_w4a16_noalloc(*args, *big[:3], 2048, 1024, 8, 4, 1, 1.0, None) == nv.NVFP4_ESCRATCH
     assert nv.moe_workspace_size(256, 64, 8, 2048, 1024) <= nv.NOALLOC_SCRATCH_BYTES   # the C5 layer fits
     assert L.nvfp4_status_string(nv.NVFP4_ESCRATCH).startswith(b"problem larger")
+    # the pre-tiled-weight variant: the same checks, and whole 128-k chunks
+    assert L.nvfp4_moe_w4a16_pretiled(*args, 4, 10, 2, 128, 128, 3, 1, 1, 1.0, None, 0, None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_moe_w4a16_pretiled(*args, 4, 8, 2, 192, 128, 4, 2, 1, 1.0, None, 0, None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_moe_w4a16_pretiled(*args, 4, 8, 2, 128, 64, 4, 2, 1, 1.0, None, 0, None) == nv.NVFP4_EINVAL
+    assert L.nvfp4_moe_w4a16_pretiled(*args, 0, 8, 2, 128, 128, 4, 2, 1, 1.0, None, 0, None) == nv.NVFP4_OK
+    assert L.nvfp4_moe_w4a16_pretiled(*args, 4, 8, 2, 128, 128, 4, 2, 1, 1.0, None, 0, None) == nv.NVFP4_EWORKSPACE
 
 
 def test_external_weight_registry_without_gpu(nv):

@@ -443,6 +443,12 @@ def test_kernel_launches_per_call(nv, oracle):
     margs = [tt(c["logits"]), tt(c["bias"]), c["x"].to(dev), *map(tt, c["w1"]), *map(tt, c["w2"])]
     mout = torch.empty((16, 64), dtype=torch.float16, device=dev)
     mws = torch.empty(nv.moe_workspace_size(16, 8, 2, 64, 64), dtype=torch.uint8, device=dev)
+    c2 = _moe_case(oracle, 16, 8, 128, 128, seed=4)
+    w1t = nv.moe_pretile_weights(tt(c2["w1"][0]), tt(c2["w1"][1]))
+    w2t = nv.moe_pretile_weights(tt(c2["w2"][0]), tt(c2["w2"][1]))
+    margs_t = [tt(c2["logits"]), tt(c2["bias"]), c2["x"].to(dev), *w1t, tt(c2["w1"][2]), *w2t, tt(c2["w2"][2])]
+    mout_t = torch.empty((16, 128), dtype=torch.float16, device=dev)
+    mws_t = torch.empty(nv.moe_workspace_size(16, 8, 2, 128, 128), dtype=torch.uint8, device=dev)
     qo = {"codes": torch.empty((64, 128), dtype=torch.uint8, device=dev),
           "sf": torch.empty((64, 16), dtype=torch.uint8, device=dev),
           "g_dec": torch.empty((64,), dtype=torch.float32, device=dev),
@@ -466,6 +472,8 @@ def test_kernel_launches_per_call(nv, oracle):
         "pretile_weight": (1, lambda s: nv.pretile_weight(d256["w_codes"], d256["w_sf"], stream=s)),
         "moe": (5, lambda s: nv.moe_w4a16(*margs, top_k=2, n_group=2, topk_group=1, out=mout, workspace=mws,
                                           stream=s)),
+        "moe_pretiled": (5, lambda s: nv.moe_w4a16_pretiled(*margs_t, top_k=2, n_group=2, topk_group=1, out=mout_t,
+                                                            workspace=mws_t, stream=s)),
         "mx_quantize_tiled": (1, lambda s: nv.mx_quantize(x, tiled=True, out=mq, stream=s)),
         "mx_tile": (1, lambda s: nv.mx_tile(mrow["codes"], mrow["sf"], stream=s)),
         "mx_gemm": (1, lambda s: nv.mx_gemm(mq, mq["g_dec"], mw, mw["g_dec"], out=my, stream=s)),

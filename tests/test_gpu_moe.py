@@ -103,3 +103,49 @@ def test_deterministic(nv, oracle):
     a = _run(nv, c, 4, 4, 2)[0]
     b = _run(nv, c, 4, 4, 2)[0]
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("T,E,top_k,n_group,topk_group,hidden,inter",
+                         [(32, 16, 4, 4, 2, 256, 128), (300, 32, 6, 4, 3, 384, 256),
+                          (200, 8, 2, 2, 2, 640, 384),     # 640 rows: the last fc2 tile past N
+                          (8, 4, 2, 1, 1, 128, 8192),      # inter at its maximum (64 fc1 row tiles)
+                          (1, 8, 2, 2, 1, 128, 128)])
+def test_pretiled_weights_bit_identical(nv, oracle, T, E, top_k, n_group, topk_group, hidden, inter):
+    # nvfp4_moe_w4a16_pretiled on moe_pretile_weights() of the same weights:
+    # the same values through the same arithmetic, only the copy layout differs
+    c = _case(oracle, T, E, hidden, inter, seed=T + E + 1)
+    dev = "cuda"
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    w1, s1, w2, s2 = t(c["w1"][0]), t(c["w1"][1]), t(c["w2"][0]), t(c["w2"][1])
+    args = (t(c["logits"]), t(c["bias"]), c["x"].to(dev))
+    kw = dict(top_k=top_k, n_group=n_group, topk_group=topk_group, want_routing=True)
+    y0, i0, w0 = nv.moe_w4a16(*args, w1, s1, t(c["w1"][2]), w2, s2, t(c["w2"][2]), **kw)
+    w1t, s1t = nv.moe_pretile_weights(w1, s1)
+    w2t, s2t = nv.moe_pretile_weights(w2, s2)
+    y1, i1, w1w = nv.moe_w4a16_pretiled(*args, w1t, s1t, t(c["w1"][2]), w2t, s2t, t(c["w2"][2]), **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(i0, i1) and torch.equal(w0.view(torch.int32), w1w.view(torch.int32))
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    rid, rw = oracle.route(c["logits"], c["bias"], top_k, n_group, topk_group, True, 1.0)
+    ref = oracle.moe_ref(c["x"].numpy(), rid, rw, *c["w1"], *c["w2"])
+    assert oracle.rel_fro(y1.cpu().double().numpy(), ref) <= TOL
+
+
+def test_pretiled_weights_full_size(nv, oracle):
+    # the benchmarked layer: pre-tiled and plain weights give the same output
+    cf = si.CONFIGS["C5"]
+    d = si.moe_inputs()
+    E, H, I = d["E"], d["hidden"], d["inter"]
+    q1 = oracle.quantize(d["w1"], group_rows=I, want_scale=False)
+    q2 = oracle.quantize(d["w2"], group_rows=H, want_scale=False)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    w1, s1 = t(q1["codes"].reshape(E, I, H // 2)), t(q1["sf"].reshape(E, I, H // 16))
+    w2, s2 = t(q2["codes"].reshape(E, H, I // 2)), t(q2["sf"].reshape(E, H, I // 16))
+    g1, g2 = t(q1["g_dec"]), t(q2["g_dec"])
+    args = (t(d["logits"]), t(d["bias"]), d["x"].cuda())
+    kw = dict(top_k=cf["top_k"], n_group=cf["n_group"], topk_group=cf["topk_group"],
+              norm_topk_prob=cf["norm_topk_prob"], routed_scaling=cf["routed_scaling"])
+    y0 = nv.moe_w4a16(*args, w1, s1, g1, w2, s2, g2, **kw)
+    y1 = nv.moe_w4a16_pretiled(*args, *nv.moe_pretile_weights(w1, s1), g1, *nv.moe_pretile_weights(w2, s2), g2, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
