@@ -84,32 +84,35 @@ MoeWs carve(void* base, int T, int E, int P, int hidden, int inter) {
 }
 
 // (value, index) pair ordering: higher value first, lower index on ties.
+// Evaluated with bitwise operations, so it compiles to compares and mask
+// operations without branches.
 __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
-  return (va > vb) || (va == vb && ia < ib);
+  return (va > vb) | ((va == vb) & (ia < ib));
 }
 
 constexpr int kMaxExpertsPerLane = 4;   // experts <= 256
 
-// One wave per token.  Each selection is made by counting, for every
-// contender, how many others come before it in the (value desc, index asc)
-// order -- the same order as taking repeated maxima with ties to the lower
-// index -- so no serial chain of cross-lane reductions is needed.
-__global__ void __launch_bounds__(256)
+// One token per workgroup of one wave; lane l holds experts l + 64 i.  Each
+// selection counts, for every contender, how many others come before it in
+// the (value desc, index asc) order -- the same order as taking repeated
+// maxima with ties to the lower index -- so no serial chain of cross-lane
+// reductions is needed.  The comparisons are branch-free and the LDS reads of
+// a phase do not depend on one another, so each phase's reads are issued
+// together; the kept groups travel as ballot masks.
+__global__ void __launch_bounds__(64)
 moe_route(const float* __restrict__ logits, const float* __restrict__ bias, int T, int E,
           int top_k, int n_group, int topk_group, int norm, float scaling,
           int32_t* __restrict__ ids, float* __restrict__ wts, uint32_t* __restrict__ pmax,
           int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
-  __shared__ float sb[4][256];      // biased scores
-  __shared__ float sg[4][256];      // group scores
-  __shared__ int kg[4][256];        // kept-group flags
-  __shared__ float cb[4][256];      // candidates (experts of kept groups): biased score
-  __shared__ int ce[4][256];        // ... and expert index, in expert order
-  __shared__ int sel_e[4][16];      // chosen experts by rank
-  __shared__ float sel_s[4][16];    // their unbiased scores
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int t_raw = blockIdx.x * (blockDim.x >> 6) + wv;
-  const bool tv = t_raw < T;             // waves past the last token idle but reach the barriers
-  const int t = tv ? t_raw : 0;
+  __shared__ float sb[64 * kMaxExpertsPerLane];   // biased scores
+  __shared__ float sg[64 * kMaxExpertsPerLane];   // group scores
+  __shared__ float cb[64 * kMaxExpertsPerLane];   // candidates (experts of kept groups): biased score
+  __shared__ int ce[64 * kMaxExpertsPerLane];     // ... and expert index, in expert order
+  __shared__ int sel_e[16];                       // chosen experts by rank
+  __shared__ float sel_s[16];                     // their unbiased scores
+  const int lane = threadIdx.x;
+  const int t = blockIdx.x;
+  if (t >= T) return;   // whole workgroup
   const float ninf = -__builtin_inff();
   const int gsize = E / n_group;
   float s[kMaxExpertsPerLane], b[kMaxExpertsPerLane];
@@ -120,14 +123,15 @@ moe_route(const float* __restrict__ logits, const float* __restrict__ bias, int 
       s[i] = sigmoid_f32(logits[(int64_t)t * E + e]);
       b[i] = s[i] + bias[e];
       if (b[i] != b[i]) b[i] = ninf;   // a NaN score ranks below every number
-      sb[wv][e] = b[i];
+      sb[e] = b[i];
     } else {
       s[i] = 0.0f;
       b[i] = ninf;
     }
   }
   __syncthreads();
-  // group scores: lane g sums its group's two best biased scores
+  // group scores: lane g sums its group's two best biased scores (one if the
+  // group has one expert)
   float gs[kMaxExpertsPerLane];
 #pragma unroll
   for (int i = 0; i < kMaxExpertsPerLane; ++i) {
@@ -136,41 +140,50 @@ moe_route(const float* __restrict__ logits, const float* __restrict__ bias, int 
     if (g < n_group) {
       float v1 = ninf, v2 = ninf;
       int i1 = -1, i2 = -1;
+      const int e0 = g * gsize;
 #pragma unroll 8
-      for (int e = g * gsize; e < (g + 1) * gsize; ++e) {
-        const float v = sb[wv][e];
-        if (i1 < 0 || better(v, e, v1, i1)) { v2 = v1; i2 = i1; v1 = v; i1 = e; }
-        else if (i2 < 0 || better(v, e, v2, i2)) { v2 = v; i2 = e; }
+      for (int j = 0; j < gsize; ++j) {
+        const int e = e0 + j;
+        const float v = sb[e];
+        const bool n1 = (i1 < 0) | better(v, e, v1, i1);
+        const bool n2 = !n1 & ((i2 < 0) | better(v, e, v2, i2));
+        v2 = n1 ? v1 : (n2 ? v : v2);
+        i2 = n1 ? i1 : (n2 ? e : i2);
+        v1 = n1 ? v : v1;
+        i1 = n1 ? e : i1;
       }
       gs[i] = (i2 >= 0) ? v1 + v2 : v1;
-      sg[wv][g] = gs[i];
+      sg[g] = gs[i];
     }
   }
   __syncthreads();
   // a group is kept when fewer than topk_group groups come before it
+  uint64_t kmask[kMaxExpertsPerLane];
 #pragma unroll
   for (int i = 0; i < kMaxExpertsPerLane; ++i) {
     const int g = lane + 64 * i;
+    bool kept = false;
     if (g < n_group) {
       int r = 0;
 #pragma unroll 8
-      for (int g2 = 0; g2 < n_group; ++g2) r += better(sg[wv][g2], g2, gs[i], g) ? 1 : 0;
-      kg[wv][g] = r < topk_group ? 1 : 0;
+      for (int g2 = 0; g2 < n_group; ++g2) r += better(sg[g2], g2, gs[i], g) ? 1 : 0;
+      kept = r < topk_group;
     }
+    kmask[i] = __ballot(kept);
   }
-  __syncthreads();
   // compact the candidates in expert order
   const uint64_t below = (1ull << lane) - 1ull;
   int nc = 0;
   bool cand[kMaxExpertsPerLane];
-  int cpos[kMaxExpertsPerLane];
 #pragma unroll
   for (int i = 0; i < kMaxExpertsPerLane; ++i) {
     const int e = lane + 64 * i;
-    cand[i] = (e < E) && kg[wv][e / gsize] != 0;
+    const int g = e / gsize;
+    const uint64_t km = g < 64 ? kmask[0] : g < 128 ? kmask[1] : g < 192 ? kmask[2] : kmask[3];
+    cand[i] = (e < E) && ((km >> (g & 63)) & 1ull);
     const uint64_t m = __ballot(cand[i]);
-    cpos[i] = nc + __popcll(m & below);
-    if (cand[i]) { cb[wv][cpos[i]] = b[i]; ce[wv][cpos[i]] = e; }
+    const int pos = nc + __popcll(m & below);
+    if (cand[i]) { cb[pos] = b[i]; ce[pos] = e; }
     nc += __popcll(m);
   }
   __syncthreads();
@@ -181,18 +194,18 @@ moe_route(const float* __restrict__ logits, const float* __restrict__ bias, int 
       const int e = lane + 64 * i;
       int r = 0;
 #pragma unroll 8
-      for (int c = 0; c < nc; ++c) r += better(cb[wv][c], ce[wv][c], b[i], e) ? 1 : 0;
-      if (r < top_k) { sel_e[wv][r] = e; sel_s[wv][r] = s[i]; }
+      for (int c = 0; c < nc; ++c) r += better(cb[c], ce[c], b[i], e) ? 1 : 0;
+      if (r < top_k) { sel_e[r] = e; sel_s[r] = s[i]; }
     }
   }
   __syncthreads();
   // normalize in rank order (every lane forms the same sequential sum), then scale
   float sum = 0.0f;
 #pragma unroll 8
-  for (int k = 0; k < top_k; ++k) sum = sum + sel_s[wv][k];
-  if (tv && lane < top_k) {
-    const float wsel = sel_s[wv][lane];
-    const int isel = sel_e[wv][lane];
+  for (int k = 0; k < top_k; ++k) sum = sum + sel_s[k];
+  if (lane < top_k) {
+    const float wsel = sel_s[lane];
+    const int isel = sel_e[lane];
     float wgt = norm ? wsel / sum : wsel;
     wgt = wgt * scaling;
     const int64_t p = (int64_t)t * top_k + lane;
@@ -759,8 +772,7 @@ hipError_t launch_moe(const MoeArgs& m, hipStream_t s) {
   const int P = m.tokens * m.top_k;
   MoeWs ws = carve(m.workspace, m.tokens, m.experts, P, m.hidden, m.inter);
   const int nt1 = fc1_tiles(m.inter);
-  // one wave (one token) per workgroup: the selection steps synchronize a
-  // single wave, not the slowest of several
+  // one wave (one token) per workgroup
   hipLaunchKernelGGL(moe_route, dim3(m.tokens), dim3(64), 0, s, m.logits, m.bias,
                      m.tokens, m.experts, m.top_k, m.n_group, m.topk_group, m.norm, m.scaling,
                      ws.ids, ws.wts, ws.pmax, m.ids_out, m.w_out);
