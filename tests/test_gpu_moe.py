@@ -80,6 +80,21 @@ def test_nan_router_logits_rank_last(nv, oracle):
     _check(oracle, nv, c, 4, 4, 2)
 
 
+@pytest.mark.parametrize("T,E,top_k,n_group,topk_group,levels",
+                         [(96, 64, 8, 8, 4, 5), (96, 64, 8, 8, 4, 1), (40, 256, 16, 16, 4, 3),
+                          (64, 32, 6, 4, 3, 2), (48, 16, 4, 16, 4, 2)])
+def test_routing_ties_resolved_by_lower_index(nv, oracle, T, E, top_k, n_group, topk_group, levels):
+    # router logits and bias drawn from a few values (levels = 1: every score
+    # equal), so biased scores, group scores and candidates tie often; both
+    # sides take the higher score first and the lower index on ties (the
+    # oracle by repeated selection, the kernel by rank counts)
+    c = _case(oracle, T, E, 64, 64, seed=T + E + levels)
+    rng = np.random.default_rng(T + E + levels)
+    c["logits"] = (rng.integers(0, levels, size=(T, E)) * 0.5).astype(np.float32)
+    c["bias"] = (rng.integers(0, levels, size=(E,)) * 0.25).astype(np.float32)
+    _check(oracle, nv, c, top_k, n_group, topk_group)
+
+
 def test_no_normalisation_and_scaling(nv, oracle):
     c = _case(oracle, 24, 16, 64, 64, seed=9)
     _check(oracle, nv, c, 4, 4, 2, norm=False, scaling=2.5)
