@@ -349,6 +349,9 @@ int oracle_route(const float* logits, const float* bias, int tokens, int experts
         else if (i2 < 0 || ranks_before(b[e], e, b[i2], i2)) { i2 = e; }
       }
       gs[g] = (i2 >= 0) ? b[i1] + b[i2] : b[i1];
+      /* a NaN group score (+inf and -inf biased scores summed) ranks below
+       * every number, as a NaN expert score does */
+      if (gs[g] != gs[g]) gs[g] = -INFINITY;
       keep[g] = 0;
     }
     /* keep topk_group groups, by repeated selection of the best remaining */

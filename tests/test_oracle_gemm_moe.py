@@ -126,6 +126,29 @@ def test_route_nan_scores_rank_last(oracle):
     assert np.all(np.isfinite(w[[0, 2]]))
 
 
+def test_route_nan_group_score_ranks_last(oracle):
+    # a group whose two best biased scores are +inf and -inf (an infinite
+    # correction bias) sums to NaN; the reading: like a NaN expert score, it
+    # ranks below every number.  Worked by hand: s = 0.5 for every expert;
+    # group scores g0 = inf + -inf -> NaN (ranks last), g1 = 0.6 + 0.5 = 1.1,
+    # g2 = 1.0, g3 = 0.7 + 0.7 = 1.4; the two kept groups are g3, g1; the
+    # best two candidates 6 and 7 (0.7, a tie: lower index first).
+    logits = np.zeros((2, 8), np.float32)
+    bias = np.array([np.inf, -np.inf, 0.1, 0.0, 0.0, 0.0, 0.2, 0.2], np.float32)
+    bias2 = bias.copy()
+    bias2[[0, 1]] = bias[[1, 0]]          # the same group with its experts swapped
+    ids, w = oracle.route(logits[:1], bias, 2, 4, 2, True, 1.0)
+    assert ids.tolist() == [[6, 7]]
+    assert np.array_equal(w, np.array([[0.5, 0.5]], np.float32))
+    ids2, _ = oracle.route(logits[:1], bias2, 2, 4, 2, True, 1.0)
+    assert ids2.tolist() == [[6, 7]]
+    # every group NaN or -inf: the lowest-index groups are kept, and the
+    # +inf experts (biased score +inf) rank first within them
+    b3 = np.array([np.inf, -np.inf, -np.inf, np.inf, np.inf, -np.inf, -np.inf, -np.inf], np.float32)
+    ids3, _ = oracle.route(logits[:1], b3, 2, 4, 2, True, 1.0)
+    assert ids3.tolist() == [[0, 3]]
+
+
 def test_route_ties_go_to_lower_index(oracle):
     logits = np.zeros((2, 16), np.float32)
     bias = np.zeros(16, np.float32)
