@@ -153,6 +153,7 @@ moe_route(const float* __restrict__ logits, const float* __restrict__ bias, int 
         i1 = n1 ? e : i1;
       }
       gs[i] = (i2 >= 0) ? v1 + v2 : v1;
+      if (gs[i] != gs[i]) gs[i] = ninf;   // +inf + -inf: a NaN group score ranks below every number
       sg[g] = gs[i];
     }
   }

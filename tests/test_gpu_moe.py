@@ -96,6 +96,22 @@ def test_routing_ties_resolved_by_lower_index(nv, oracle, T, E, top_k, n_group, 
     _check(oracle, nv, c, top_k, n_group, topk_group)
 
 
+def test_infinite_bias_matches_oracle(nv, oracle):
+    # +inf / -inf correction biases and NaN logits: infinite biased scores,
+    # and groups whose two best sum to NaN (ranked below every number on both
+    # sides); ids exact, weights bit for bit
+    c = _case(oracle, 64, 32, 64, 64, seed=33)
+    rng = np.random.default_rng(33)
+    bias = c["bias"].copy()
+    bias[[0, 5, 9, 20]] = np.inf
+    bias[[1, 4, 8, 21, 30]] = -np.inf
+    lg = c["logits"].copy()
+    lg[rng.random(lg.shape) < 0.05] = np.nan
+    c["bias"], c["logits"] = bias, lg
+    # two experts per group: groups {0, 1}, {4, 5}, {8, 9}, {20, 21} sum +inf and -inf
+    _check(oracle, nv, c, 4, 16, 4)
+
+
 def test_no_normalisation_and_scaling(nv, oracle):
     c = _case(oracle, 24, 16, 64, 64, seed=9)
     _check(oracle, nv, c, 4, 4, 2, norm=False, scaling=2.5)
