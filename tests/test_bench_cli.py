@@ -1,5 +1,5 @@
 """bench.py contract on the host: more than one GPU is refused with a message
-(this build measures one GPU), before any GPU is touched."""
+(the benchmark measures one GPU), before any GPU is touched."""
 import os
 import subprocess
 import sys
